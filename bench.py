@@ -1,0 +1,195 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of seeded synthetic input: for the ring-share workload
+(B1 H32, 16384 local query rows against 131072 keys streamed as 8 chunks of 16384, bf16, d128, the last
+chunk causal) that is 8 forward launches into fp32 partials and 7 merges, the last writing bf16 O and
+the fp32 LSE.  Inputs are resident in HBM before the timed region.  Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+`value` is attention TFLOP/s of the whole step (algorithmic FLOPs: 4*d per visible query/key pair, a square
+causal block counted as N^2/2) over the step time.  The `roofline` object covers the dominant kernel (the
+forward launches), timed with HIP events that the library records on the stream the kernels run on.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+METRIC = "attn fwd TFLOP/s and % of MI355X bf16 MFMA peak; merge GB/s vs HBM peak"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def merge_bytes(w) -> float:
+    """Algorithmic HBM bytes of the merges of one chunked step: per row, read two partial rows and lse
+    values, write one row and one lse.  All but the last merge are fp32 -> fp32; the last writes bf16."""
+    rows = w.B * w.H * w.N_q
+    n = w.chunks - 1
+    f32_merge = rows * (w.d * (4 + 4 + 4) + 12)
+    last = rows * (w.d * (4 + 4 + (2 if w.dtype == "bf16" else 4)) + 12)
+    return (n - 1) * f32_merge + last if n >= 1 else 0.0
+
+
+def cpu_baseline(w, seconds: float):
+    """Time the fp64 oracle (blockwise form, key blocks of 1024, row blocks of 256) on a bounded sample:
+    row blocks of head (0,0) against all keys, run on a thread pool with one BLAS thread per worker."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import workloads as W
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    k = W.head_f64(w, W.K_T, 0, 0)
+    v = W.head_f64(w, W.V_T, 0, 0)
+    q = W.head_f64(w, W.Q_T, 0, 0)
+    rb = 256
+    starts = list(range(0, w.N_q, rb))
+    # probe one block to size the sample to about `seconds` of wall time
+    with threadpool_limits(limits=1, user_api="blas"):
+        t0 = time.perf_counter()
+        oracle.blockwise_head(q[:rb], k, v, w.scale, w.causal, w.offset, np.arange(rb), 1024)
+        one = time.perf_counter() - t0
+        nblk = int(max(1, min(len(starts), round(seconds / one * workers))))
+        # spread the sampled blocks evenly over the query range (causal rows differ in cost)
+        pick = [starts[int(i * len(starts) / nblk)] for i in range(nblk)]
+
+        def run(s):
+            rows = np.arange(s, min(s + rb, w.N_q))
+            oracle.blockwise_head(q[rows], k, v, w.scale, w.causal, w.offset, rows, 1024)
+            return rows
+
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(workers) as ex:
+            done = list(ex.map(run, pick))
+        dt = time.perf_counter() - t0
+    rows = np.concatenate(done)
+    vis = np.minimum(w.N_kv, rows + w.offset + 1) if w.causal else np.full(len(rows), w.N_kv)
+    flops = 4.0 * w.d * float(vis.sum())
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+        "sample": f"fp64 blockwise oracle, head (0,0), {len(rows)} query rows in {nblk} blocks of {rb} spread over "
+                  f"the {w.N_q} rows, each against all {w.N_kv} keys ({flops:.3e} FLOP in {dt:.1f} s)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="ring_share_128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the path is one device's share); --gpus {args.gpus} is not "
+              "supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_blockwise_attention_fwd_amd as A
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    A.lib()
+    w = W.WORKLOADS[args.workload]
+    log(f"workload {w}")
+    t0 = time.time()
+
+    def dev(t):
+        import numpy as np
+        s = W.tensor_storage(w, t)
+        if s.dtype == np.uint16:
+            return torch.from_numpy(s.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(s).cuda()
+
+    q, k, v = dev(W.Q_T), dev(W.K_T), dev(W.V_T)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N_q), dtype=torch.float32, device="cuda")
+    ws_n = A.workspace_bytes(w.B, w.H, w.N_q, w.d, w.chunks)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log(f"inputs resident in {time.time() - t0:.1f} s")
+
+    def step():
+        if w.chunks > 1:
+            A.fwd_chunked(q, k, v, w.chunks, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=ws)
+        else:
+            A.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    A.timing_enable(True)
+    A.timing_read()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    A.timing_enable(False)
+    kt = A.timing_read()
+    total_ms = e0.elapsed_time(e1)
+    ms = total_ms / args.steps
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step; kernels {kt}")
+
+    flops = w.flops()
+    value = flops / (ms * 1e-3) / 1e12
+    n_fwd, fwd_ms = kt["fwd"]
+    n_mrg, mrg_ms = kt["merge"]
+    fwd_tflops = flops * args.steps / (fwd_ms * 1e-3) / 1e12 if fwd_ms > 0 else None
+    mb = merge_bytes(w)
+    merge_gbs = mb * args.steps / (mrg_ms * 1e-3) / 1e9 if mrg_ms > 0 else None
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N_q": w.N_q, "N_kv": w.N_kv, "d": w.d,
+                   "causal": w.causal, "chunks": w.chunks, "scale": w.scale, "parallelism": "single-gpu"},
+        "pct_bf16_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
+        "fwd_kernel": {"launches_per_step": n_fwd / args.steps, "ms_per_step": fwd_ms / args.steps,
+                       "tflops": None if fwd_tflops is None else round(fwd_tflops, 2)},
+        "merge": None if merge_gbs is None else {
+            "launches_per_step": n_mrg / args.steps, "ms_per_step": mrg_ms / args.steps,
+            "bytes_per_step": mb, "gbs": round(merge_gbs, 1), "pct_hbm_peak": round(100 * merge_gbs / HBM_PEAK_GBS, 2)},
+        "roofline": {"bound": "mfma", "achieved": None if fwd_tflops is None else round(fwd_tflops, 2),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": None if fwd_tflops is None else round(fwd_tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    if w.dtype != "bf16":
+        out["roofline"]["bound"] = "alu"
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

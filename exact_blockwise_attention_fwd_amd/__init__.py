@@ -1,0 +1,185 @@
+"""Exact blockwise attention forward and (O, lse) merge on MI355X: Python binding of libattn.so.
+
+The binding only marshals arguments: it turns torch tensors into device pointers and the current HIP
+stream, calls the C ABI declared in ``include/attn.h``, and raises ``AttnError`` on a non-zero status.
+Every step of the computation runs in the library's HIP kernels; torch only provides device memory and
+streams.  If the library has not been built, every call raises (there is no fallback).
+
+    o, lse = fwd(q, k, v, causal=True)                # q, k, v: [B, H, N, d] cuda tensors, bf16 or fp32
+    o, lse = fwd_chunked(q, k, v, chunks=8, causal=True)
+    o, lse = merge(o_a, lse_a, o_b, lse_b)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+ATTN_F32, ATTN_BF16 = 0, 1
+STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL_PTR", 2: "ATTN_ERR_BAD_SHAPE", 3: "ATTN_ERR_UNSUPPORTED_D",
+          4: "ATTN_ERR_BAD_DTYPE", 5: "ATTN_ERR_BAD_SCALE", 6: "ATTN_ERR_WORKSPACE_TOO_SMALL",
+          7: "ATTN_ERR_BAD_ALIAS", 8: "ATTN_ERR_HIP", 9: "ATTN_ERR_MISALIGNED"}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        self.status = status
+        super().__init__(f"{func}: {STATUS.get(status, status)} ({detail})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libattn.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m exact_blockwise_attention_fwd_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, ll, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_longlong, ctypes.c_size_t
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    L.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, ll, ll, i, i, vp]
+    L.attn_merge.argtypes = [vp, vp, vp, vp, vp, vp, ll, i, i, i, vp]
+    L.attn_fwd_chunked_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.attn_fwd_chunked_workspace_bytes.restype = sz
+    L.attn_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp]
+    L.attn_strerror.argtypes = [i]
+    L.attn_strerror.restype = ctypes.c_char_p
+    L.attn_last_error.argtypes = []
+    L.attn_last_error.restype = ctypes.c_char_p
+    L.attn_timing_enable.argtypes = [i]
+    L.attn_timing_read.argtypes = [ctypes.POINTER(ll), ctypes.POINTER(ctypes.c_double)]
+    for name in ("attn_fwd", "attn_fwd_ex", "attn_merge", "attn_fwd_chunked", "attn_timing_enable",
+                 "attn_timing_read"):
+        getattr(L, name).restype = i
+    _lib = L
+    return L
+
+
+def _check(status: int, func: str):
+    if status != 0:
+        raise AttnError(status, func, lib().attn_last_error().decode())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _torch_dtype(code: int):
+    import torch
+    return torch.bfloat16 if code == ATTN_BF16 else torch.float32
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """Exact attention over all keys.  q [B,H,N_q,d], k and v [B,H,N_kv,d] -> (o [B,H,N_q,d], lse fp32)."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n)
+    B, H, N_q, d = q.shape
+    N_kv = k.shape[2]
+    dt = _dtype_code(q)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                          B, H, N_q, N_kv, d, int(causal), scale, dt, _stream(q)), "attn_fwd")
+    return out, lse
+
+
+def fwd_ex(q, k, v, causal: bool = False, scale: float | None = None, causal_offset: int | None = None,
+           key_range: tuple[int, int] | None = None, out_dtype=None, out=None, lse=None):
+    """Attention of q against keys [lo, hi) of k and v with an explicit causal offset and output dtype."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n)
+    B, H, N_q, d = q.shape
+    n_total = k.shape[2]
+    lo, hi = key_range if key_range is not None else (0, n_total)
+    if not (0 <= lo <= hi <= n_total):
+        raise ValueError(f"key_range {key_range} outside [0, {n_total}]")
+    dt = _dtype_code(q)
+    odt = dt if out_dtype is None else _dtype_code(torch.empty(0, dtype=out_dtype))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    offset = (hi - lo) - N_q if causal_offset is None else int(causal_offset)
+    out = torch.empty((B, H, N_q, d), dtype=_torch_dtype(odt), device=q.device) if out is None else out
+    lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    es = q.element_size()
+    _check(lib().attn_fwd_ex(q.data_ptr(), k.data_ptr() + lo * d * es, v.data_ptr() + lo * d * es,
+                             out.data_ptr(), lse.data_ptr(), B, H, N_q, hi - lo, d, int(causal), scale,
+                             offset, n_total * d, dt, odt, _stream(q)), "attn_fwd_ex")
+    return out, lse
+
+
+def merge(o_a, lse_a, o_b, lse_b, out=None, lse=None, out_dtype=None):
+    """Combine two partial results (o [..., d], lse [...]) over disjoint key sets."""
+    import torch
+    for t, n in ((o_a, "o_a"), (lse_a, "lse_a"), (o_b, "o_b"), (lse_b, "lse_b")):
+        _need(t, n)
+    d = o_a.shape[-1]
+    rows = lse_a.numel()
+    dt = _dtype_code(o_a)
+    odt = dt if out_dtype is None else _dtype_code(torch.empty(0, dtype=out_dtype))
+    out = torch.empty(o_a.shape, dtype=_torch_dtype(odt), device=o_a.device) if out is None else out
+    lse = torch.empty_like(lse_a) if lse is None else lse
+    _check(lib().attn_merge(o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(), lse_b.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), rows, d, dt, odt, _stream(o_a)), "attn_merge")
+    return out, lse
+
+
+def workspace_bytes(B: int, H: int, N_q: int, d: int, chunks: int) -> int:
+    return int(lib().attn_fwd_chunked_workspace_bytes(B, H, N_q, d, chunks))
+
+
+def fwd_chunked(q, k, v, chunks: int, causal: bool = False, scale: float | None = None, out=None, lse=None,
+                workspace=None):
+    """Keys cut into `chunks` contiguous chunks, each attended separately and folded through the merge."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n)
+    B, H, N_q, d = q.shape
+    N_kv = k.shape[2]
+    dt = _dtype_code(q)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    need = workspace_bytes(B, H, N_q, d, chunks)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().attn_fwd_chunked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                  B, H, N_q, N_kv, d, int(causal), scale, int(chunks), dt, ws_ptr, ws_n,
+                                  _stream(q)), "attn_fwd_chunked")
+    return out, lse
+
+
+def timing_enable(on: bool = True):
+    _check(lib().attn_timing_enable(int(on)), "attn_timing_enable")
+
+
+def timing_read():
+    """{'fwd': (launches, total_ms), 'merge': (launches, total_ms)} since the last read."""
+    counts = (ctypes.c_longlong * 2)()
+    ms = (ctypes.c_double * 2)()
+    _check(lib().attn_timing_read(counts, ms), "attn_timing_read")
+    return {"fwd": (counts[0], ms[0]), "merge": (counts[1], ms[1])}

@@ -1,0 +1,364 @@
+// C-ABI front end of libattn.so (declared in include/attn.h): argument validation before any HIP call,
+// kernel dispatch by dtype and head dimension, the chunked driver, and opt-in launch timing.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "attn.h"
+#include "attn_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+bool debug_sync() {
+    static const bool on = [] {
+        const char* e = getenv("ATTN_DEBUG");
+        return e && e[0] == '1';
+    }();
+    return on;
+}
+
+// ---------------------------------------------------------------------------------------- launch timing
+struct Timed {
+    int kind;
+    hipEvent_t start, stop;
+};
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<Timed> g_timed;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+    if (!g_event_pool.empty()) {
+        hipEvent_t e = g_event_pool.back();
+        g_event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Runs one launch with optional timing and debug synchronisation; maps HIP failures to ATTN_ERR_HIP.
+template <class F>
+int run(int kind, hipStream_t s, const char* what, F&& launch) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    bool timed = false;
+    {
+        std::lock_guard<std::mutex> g(g_timing_mu);
+        if (g_timing_on) {
+            e0 = take_event();
+            e1 = take_event();
+            timed = e0 && e1;
+        }
+    }
+    if (timed && hipEventRecord(e0, s) != hipSuccess) return fail(ATTN_ERR_HIP, "%s: hipEventRecord failed", what);
+    hipError_t err = launch();
+    if (err != hipSuccess) return fail(ATTN_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(err));
+    if (timed) {
+        if (hipEventRecord(e1, s) != hipSuccess) return fail(ATTN_ERR_HIP, "%s: hipEventRecord failed", what);
+        std::lock_guard<std::mutex> g(g_timing_mu);
+        g_timed.push_back({kind, e0, e1});
+    }
+    if (debug_sync()) {
+        err = hipStreamSynchronize(s);
+        if (err != hipSuccess) return fail(ATTN_ERR_HIP, "%s: kernel failed: %s", what, hipGetErrorString(err));
+    }
+    return ATTN_OK;
+}
+
+// ------------------------------------------------------------------------------------------- validation
+size_t esize(attn_dtype t) { return t == ATTN_BF16 ? 2 : 4; }
+bool valid_dtype(int t) { return t == ATTN_F32 || t == ATTN_BF16; }
+
+bool overlap(const void* a, size_t an, const void* b, size_t bn) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return an && bn && x < y + bn && y < x + an;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+struct FwdCheck {
+    size_t q_bytes, kv_bytes, o_bytes, lse_bytes;
+    long long kv_stride;
+};
+
+int check_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q,
+              int N_kv, int d, float scale, long long kv_head_stride, int in_dtype, int out_dtype,
+              FwdCheck* out) {
+    if (!Q || !K || !V || !O || !LSE) return fail(ATTN_ERR_NULL_PTR, "Q, K, V, O and LSE must be non-NULL");
+    if (B < 1 || H < 1 || N_q < 1 || N_kv < 1)
+        return fail(ATTN_ERR_BAD_SHAPE, "B, H, N_q, N_kv must be >= 1 (got %d, %d, %d, %d)", B, H, N_q, N_kv);
+    if ((long long)B * H > 0x7fffffffLL) return fail(ATTN_ERR_BAD_SHAPE, "B*H exceeds 2^31-1");
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+        return fail(ATTN_ERR_BAD_DTYPE, "unknown dtype (%d, %d)", in_dtype, out_dtype);
+    if (out_dtype != ATTN_F32 && out_dtype != in_dtype)
+        return fail(ATTN_ERR_BAD_DTYPE, "output dtype must be fp32 or the input dtype");
+    if (in_dtype == ATTN_BF16 && d != 64 && d != 128)
+        return fail(ATTN_ERR_UNSUPPORTED_D, "bf16 attention supports d = 64 or 128 (got %d)", d);
+    if (in_dtype == ATTN_F32 && (d < 1 || d > 256))
+        return fail(ATTN_ERR_UNSUPPORTED_D, "fp32 attention supports 1 <= d <= 256 (got %d)", d);
+    if (!isfinite(scale)) return fail(ATTN_ERR_BAD_SCALE, "scale must be finite");
+    const long long head = (long long)N_kv * d;
+    const long long stride = kv_head_stride == 0 ? head : kv_head_stride;
+    if (stride < head)
+        return fail(ATTN_ERR_BAD_SHAPE, "kv_head_stride %lld is smaller than N_kv*d = %lld", stride, head);
+    const long long bh = (long long)B * H;
+    const size_t ei = esize((attn_dtype)in_dtype), eo = esize((attn_dtype)out_dtype);
+    out->q_bytes = (size_t)(bh * N_q * d) * ei;
+    out->kv_bytes = (size_t)((bh - 1) * stride + head) * ei;
+    out->o_bytes = (size_t)(bh * N_q * d) * eo;
+    out->lse_bytes = (size_t)(bh * N_q) * sizeof(float);
+    out->kv_stride = stride;
+    if (in_dtype == ATTN_BF16) {
+        if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || (stride % 8) != 0)
+            return fail(ATTN_ERR_MISALIGNED, "bf16 attention needs 16-byte aligned Q, K, V, O and head strides");
+    } else if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 3) {
+        return fail(ATTN_ERR_MISALIGNED, "fp32 attention needs 4-byte aligned Q, K, V, O");
+    }
+    if (((uintptr_t)LSE & 3) != 0) return fail(ATTN_ERR_MISALIGNED, "LSE must be 4-byte aligned");
+    const void* ins[3] = {Q, K, V};
+    const size_t in_n[3] = {out->q_bytes, out->kv_bytes, out->kv_bytes};
+    for (int i = 0; i < 3; ++i) {
+        if (overlap(O, out->o_bytes, ins[i], in_n[i]))
+            return fail(ATTN_ERR_BAD_ALIAS, "O overlaps an input (Q, K or V)");
+        if (overlap(LSE, out->lse_bytes, ins[i], in_n[i]))
+            return fail(ATTN_ERR_BAD_ALIAS, "LSE overlaps an input (Q, K or V)");
+    }
+    if (overlap(O, out->o_bytes, LSE, out->lse_bytes)) return fail(ATTN_ERR_BAD_ALIAS, "O overlaps LSE");
+    return ATTN_OK;
+}
+
+int clamp_offset(long long off, int N_q, int N_kv) {
+    if (off > N_kv) off = N_kv;
+    if (off < -(long long)N_q - 1) off = -(long long)N_q - 1;
+    return (int)off;
+}
+
+int launch_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q,
+               int N_kv, int d, int causal, float scale, long long offset, long long kv_stride, int in_dtype,
+               int out_dtype, hipStream_t s) {
+    attn::FwdArgs a;
+    a.q = Q;
+    a.k = K;
+    a.v = V;
+    a.o = O;
+    a.lse = LSE;
+    a.q_head_stride = (long long)N_q * d;
+    a.kv_head_stride = kv_stride;
+    a.n_q = N_q;
+    a.n_kv = N_kv;
+    a.d = d;
+    a.bh = B * H;
+    a.causal = causal ? 1 : 0;
+    a.offset = causal ? clamp_offset(offset, N_q, N_kv) : N_kv;
+    a.scale = scale;
+    if (in_dtype == ATTN_BF16)
+        return run(0, s, "attn_fwd(bf16)", [&] { return attn::launch_fwd_bf16(a, out_dtype == ATTN_F32, s); });
+    return run(0, s, "attn_fwd(fp32)", [&] { return attn::launch_fwd_f32(a, s); });
+}
+
+int launch_merge(const void* O_a, const float* lse_a, const void* O_b, const float* lse_b, void* O, float* lse,
+                 long long rows, int d, int in_dtype, int out_dtype, hipStream_t s) {
+    attn::MergeArgs m;
+    m.o_a = O_a;
+    m.lse_a = lse_a;
+    m.o_b = O_b;
+    m.lse_b = lse_b;
+    m.o = O;
+    m.lse = lse;
+    m.rows = rows;
+    m.d = d;
+    m.in_bf16 = in_dtype == ATTN_BF16;
+    m.out_bf16 = out_dtype == ATTN_BF16;
+    return run(1, s, "attn_merge", [&] { return attn::launch_merge(m, s); });
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_strerror(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL_PTR: return "null pointer";
+        case ATTN_ERR_BAD_SHAPE: return "bad shape";
+        case ATTN_ERR_UNSUPPORTED_D: return "unsupported head dimension";
+        case ATTN_ERR_BAD_DTYPE: return "bad dtype";
+        case ATTN_ERR_BAD_SCALE: return "bad scale";
+        case ATTN_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case ATTN_ERR_BAD_ALIAS: return "forbidden aliasing";
+        case ATTN_ERR_HIP: return "HIP error";
+        case ATTN_ERR_MISALIGNED: return "misaligned pointer";
+        default: return "unknown status";
+    }
+}
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+int attn_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q, int N_kv,
+                int d, int causal, float scale, long long causal_offset, long long kv_head_stride,
+                attn_dtype in_dtype, attn_dtype out_dtype, void* hip_stream) {
+    g_last_error.clear();
+    FwdCheck c;
+    int st = check_fwd(Q, K, V, O, LSE, B, H, N_q, N_kv, d, scale, kv_head_stride, in_dtype, out_dtype, &c);
+    if (st) return st;
+    return launch_fwd(Q, K, V, O, LSE, B, H, N_q, N_kv, d, causal, scale, causal_offset, c.kv_stride, in_dtype,
+                      out_dtype, (hipStream_t)hip_stream);
+}
+
+int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q, int N_kv,
+             int d, int causal, float scale, attn_dtype dtype, void* hip_stream) {
+    return attn_fwd_ex(Q, K, V, O, LSE, B, H, N_q, N_kv, d, causal, scale, (long long)N_kv - N_q, 0, dtype, dtype,
+                       hip_stream);
+}
+
+int attn_merge(const void* O_a, const float* lse_a, const void* O_b, const float* lse_b, void* O, float* lse,
+               long long rows, int d, attn_dtype in_dtype, attn_dtype out_dtype, void* hip_stream) {
+    g_last_error.clear();
+    if (!O_a || !lse_a || !O_b || !lse_b || !O || !lse) return fail(ATTN_ERR_NULL_PTR, "merge pointers must be non-NULL");
+    if (rows < 1 || d < 1) return fail(ATTN_ERR_BAD_SHAPE, "rows and d must be >= 1 (got %lld, %d)", rows, d);
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(ATTN_ERR_BAD_DTYPE, "unknown dtype");
+    if (rows > (1LL << 40) / d) return fail(ATTN_ERR_BAD_SHAPE, "rows*d too large");
+    const size_t in_b = (size_t)rows * d * esize(in_dtype), out_b = (size_t)rows * d * esize(out_dtype);
+    const size_t lse_b_n = (size_t)rows * sizeof(float);
+    if ((((uintptr_t)O_a | (uintptr_t)O_b | (uintptr_t)O) & (esize(in_dtype) - 1)) ||
+        ((uintptr_t)O & (esize(out_dtype) - 1)) || (((uintptr_t)lse_a | (uintptr_t)lse_b | (uintptr_t)lse) & 3))
+        return fail(ATTN_ERR_MISALIGNED, "merge buffers must be aligned to their element size");
+    // O may be exactly O_a or O_b (same dtype); any other overlap with an input is forbidden
+    const bool same_t = in_dtype == out_dtype;
+    for (const void* src : {O_a, O_b}) {
+        if (O == src) {
+            if (!same_t) return fail(ATTN_ERR_BAD_ALIAS, "in-place merge needs equal input and output dtypes");
+        } else if (overlap(O, out_b, src, in_b)) {
+            return fail(ATTN_ERR_BAD_ALIAS, "O partially overlaps O_a or O_b");
+        }
+    }
+    for (const float* src : {lse_a, lse_b})
+        if (lse != src && overlap(lse, lse_b_n, src, lse_b_n))
+            return fail(ATTN_ERR_BAD_ALIAS, "lse partially overlaps lse_a or lse_b");
+    for (const void* p : {(const void*)lse_a, (const void*)lse_b, (const void*)lse})
+        if (overlap(O, out_b, p, lse_b_n)) return fail(ATTN_ERR_BAD_ALIAS, "O overlaps an lse array");
+    for (const void* p : {O_a, O_b})
+        if (overlap(lse, lse_b_n, p, in_b)) return fail(ATTN_ERR_BAD_ALIAS, "lse overlaps O_a or O_b");
+    return launch_merge(O_a, lse_a, O_b, lse_b, O, lse, rows, d, in_dtype, out_dtype, (hipStream_t)hip_stream);
+}
+
+size_t attn_fwd_chunked_workspace_bytes(int B, int H, int N_q, int d, int P) {
+    if (B < 1 || H < 1 || N_q < 1 || d < 1 || P < 1) return 0;
+    if (P == 1) return 0;
+    const size_t rows = (size_t)B * H * N_q;
+    return 2 * align256(rows * d * sizeof(float)) + 2 * align256(rows * sizeof(float));
+}
+
+int attn_fwd_chunked(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q,
+                     int N_kv, int d, int causal, float scale, int P, attn_dtype dtype, void* workspace,
+                     size_t workspace_bytes, void* hip_stream) {
+    g_last_error.clear();
+    FwdCheck c;
+    int st = check_fwd(Q, K, V, O, LSE, B, H, N_q, N_kv, d, scale, 0, dtype, dtype, &c);
+    if (st) return st;
+    if (P < 1) return fail(ATTN_ERR_BAD_SHAPE, "P must be >= 1 (got %d)", P);
+    hipStream_t s = (hipStream_t)hip_stream;
+    const long long offset = (long long)N_kv - N_q;
+    if (P == 1)
+        return launch_fwd(Q, K, V, O, LSE, B, H, N_q, N_kv, d, causal, scale, offset, c.kv_stride, dtype, dtype, s);
+
+    const size_t need = attn_fwd_chunked_workspace_bytes(B, H, N_q, d, P);
+    if (!workspace || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+    if (((uintptr_t)workspace & 255) != 0) return fail(ATTN_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+    const void* others[5] = {Q, K, V, O, LSE};
+    const size_t other_n[5] = {c.q_bytes, c.kv_bytes, c.kv_bytes, c.o_bytes, c.lse_bytes};
+    for (int i = 0; i < 5; ++i)
+        if (overlap(workspace, need, others[i], other_n[i]))
+            return fail(ATTN_ERR_BAD_ALIAS, "workspace overlaps Q, K, V, O or LSE");
+
+    // chunk p covers keys [floor(p*N_kv/P), floor((p+1)*N_kv/P)); empty or wholly-future chunks are skipped
+    std::vector<int> live;
+    for (int p = 0; p < P; ++p) {
+        const long long lo = (long long)p * N_kv / P, hi = (long long)(p + 1) * N_kv / P;
+        if (hi == lo) continue;
+        if (causal && (long long)N_q - 1 + offset - lo < 0) continue;
+        live.push_back(p);
+    }
+    if (live.empty()) live.push_back(0);   // unreachable with offset N_kv - N_q; kept for safety
+    const size_t rows = (size_t)B * H * N_q;
+    char* ws = static_cast<char*>(workspace);
+    float* o_acc = reinterpret_cast<float*>(ws);
+    float* o_p = reinterpret_cast<float*>(ws + align256(rows * d * sizeof(float)));
+    float* lse_acc = reinterpret_cast<float*>(ws + 2 * align256(rows * d * sizeof(float)));
+    float* lse_p = reinterpret_cast<float*>(ws + 2 * align256(rows * d * sizeof(float)) + align256(rows * sizeof(float)));
+    const size_t es = esize(dtype);
+    auto chunk = [&](int p, void* o, float* lse, attn_dtype out_t) {
+        const long long lo = (long long)p * N_kv / P, hi = (long long)(p + 1) * N_kv / P;
+        const char* kp = static_cast<const char*>(K) + lo * d * es;
+        const char* vp = static_cast<const char*>(V) + lo * d * es;
+        return launch_fwd(Q, kp, vp, o, lse, B, H, N_q, (int)(hi - lo), d, causal, scale, offset - lo, c.kv_stride,
+                          dtype, out_t, s);
+    };
+    if (live.size() == 1) return chunk(live[0], O, LSE, dtype);
+    if ((st = chunk(live[0], o_acc, lse_acc, ATTN_F32))) return st;
+    for (size_t i = 1; i < live.size(); ++i) {
+        if ((st = chunk(live[i], o_p, lse_p, ATTN_F32))) return st;
+        const bool last = i + 1 == live.size();
+        st = last ? launch_merge(o_acc, lse_acc, o_p, lse_p, O, LSE, (long long)rows, d, ATTN_F32, dtype, s)
+                  : launch_merge(o_acc, lse_acc, o_p, lse_p, o_acc, lse_acc, (long long)rows, d, ATTN_F32, ATTN_F32, s);
+        if (st) return st;
+    }
+    return ATTN_OK;
+}
+
+int attn_timing_enable(int on) {
+    std::lock_guard<std::mutex> g(g_timing_mu);
+    g_timing_on = on != 0;
+    return ATTN_OK;
+}
+
+int attn_timing_read(long long counts[2], double total_ms[2]) {
+    std::vector<Timed> recs;
+    {
+        std::lock_guard<std::mutex> g(g_timing_mu);
+        recs.swap(g_timed);
+    }
+    counts[0] = counts[1] = 0;
+    total_ms[0] = total_ms[1] = 0.0;
+    int st = ATTN_OK;
+    for (const Timed& r : recs) {
+        float ms = 0.f;
+        if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) {
+            st = fail(ATTN_ERR_HIP, "attn_timing_read: event query failed");
+        } else if (r.kind == 0 || r.kind == 1) {
+            counts[r.kind] += 1;
+            total_ms[r.kind] += ms;
+        }
+    }
+    std::lock_guard<std::mutex> g(g_timing_mu);
+    for (const Timed& r : recs) {
+        g_event_pool.push_back(r.start);
+        g_event_pool.push_back(r.stop);
+    }
+    return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// Internal interface between the C-ABI front end (attn_api.hip) and the kernels.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace attn {
+
+// One forward launch over a key range.  All strides and offsets are in elements.
+struct FwdArgs {
+    const void* q;          // [bh][n_q][d], head stride q_head_stride
+    const void* k;          // first key of the range, head stride kv_head_stride
+    const void* v;
+    void* o;                // [bh][n_q][d], same head stride as q
+    float* lse;             // [bh][n_q]
+    long long q_head_stride;
+    long long kv_head_stride;
+    int n_q, n_kv, d, bh;
+    int causal;
+    int offset;             // key j visible to query i iff j <= i + offset (clamped to [-n_q-1, n_kv])
+    float scale;            // signed logit scale
+};
+
+struct MergeArgs {
+    const void* o_a;
+    const float* lse_a;
+    const void* o_b;
+    const float* lse_b;
+    void* o;
+    float* lse;
+    long long rows;
+    int d;
+    int in_bf16, out_bf16;
+};
+
+// bf16 inputs, fp32 accumulation; d in {64, 128}; O in bf16 or fp32.
+hipError_t launch_fwd_bf16(const FwdArgs& a, bool out_f32, hipStream_t s);
+// fp32 inputs and output; 1 <= d <= 256.
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+
+}  // namespace attn

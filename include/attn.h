@@ -1,0 +1,143 @@
+/*
+ * attn.h - C ABI of libattn.so: exact blockwise attention forward and the (O, lse) merge on MI355X (gfx950).
+ *
+ * What is computed.  For every batch b and head h, with Q [N_q, d], K and V [N_kv, d]:
+ *     S = scale * Q K^T,   P = row-softmax(S) over the visible keys,   O = P V,
+ *     LSE_i = ln sum_{j visible} exp(S_ij).
+ * This is the attention of "FlashAttention by hand" (paragraph on the three standard steps), computed the
+ * way that page describes it (paragraphs on online softmax, the per-tile flow, rescaling and the final
+ * division): key/value tiles stream through on-chip memory while each query row keeps a running max, a
+ * running denominator and an unnormalised output; the N_q x N_kv score matrix is never written to memory.
+ * The merge combines two partial results over disjoint key sets, the associative step of the
+ * "ATTENTION2D" explainer (sections 2 and 3) that Ring Attention ("Ring Attention with Blockwise Parallel
+ * Transformers" explainer, section 3) needs when key/value blocks arrive one after another.
+ *
+ * Conventions that hold for every entry point.
+ *   Layout     Q, K, V, O are [B, H, N, d] row-major (d fastest, contiguous); LSE is [B, H, N_q] fp32.
+ *   Causal     bottom-right aligned ("HOF SWIFT Attention", section 3, Transform stage, names causal
+ *              masking without fixing the alignment): key j is visible to query i iff j <= i + offset,
+ *              where offset = N_kv - N_q unless given explicitly.  Non-causal: every key is visible.
+ *   Empty row  a query with no visible key gets O = 0 and LSE = -inf (the identity of the merge).
+ *   LSE        natural log, includes the scale.
+ *   Dtypes     ATTN_BF16: Q, K, V in bf16, fp32 accumulation and statistics, O rounded to bf16 (RNE);
+ *              ATTN_F32: fp32 everywhere.  The input dtype picks the kernel; d in {64, 128} for bf16,
+ *              1..256 for fp32.
+ *   Ownership  the caller allocates and owns every buffer (device memory), including the chunked
+ *              workspace; the library never allocates device memory and keeps no per-call state.
+ *   Streams    every call enqueues on `hip_stream` (a hipStream_t; NULL = the null stream) and returns
+ *              without synchronising.  Faults inside kernels surface at the caller's next synchronise.
+ *              With the environment variable ATTN_DEBUG=1 every launch is followed by a synchronise and
+ *              an error check.
+ *   Errors     the return value is an attn_status.  Every argument is validated before any HIP call, so
+ *              a non-zero status means nothing was enqueued (except ATTN_ERR_HIP, reported after a failed
+ *              launch).  attn_strerror() names a status; attn_last_error() describes the last failure on
+ *              the calling thread.
+ *   Aliasing   O and LSE must not overlap Q, K, V, each other, or the workspace.
+ *   Sizes      B, H, N_q, N_kv >= 1; element offsets are 64-bit.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL_PTR = 1,           /* a required pointer is NULL */
+    ATTN_ERR_BAD_SHAPE = 2,          /* B, H, N_q, N_kv, rows or P out of range, or a stride too small */
+    ATTN_ERR_UNSUPPORTED_D = 3,      /* head dimension not supported for this dtype */
+    ATTN_ERR_BAD_DTYPE = 4,          /* unknown dtype or unsupported dtype combination */
+    ATTN_ERR_BAD_SCALE = 5,          /* scale is NaN or infinite */
+    ATTN_ERR_WORKSPACE_TOO_SMALL = 6,/* chunked mode: workspace NULL or smaller than required */
+    ATTN_ERR_BAD_ALIAS = 7,          /* outputs overlap inputs (or each other) where that is not allowed */
+    ATTN_ERR_HIP = 8,                /* a HIP launch or runtime call failed */
+    ATTN_ERR_MISALIGNED = 9          /* a pointer or stride is not aligned as the kernel needs (bf16: 16 bytes
+                                        for Q, K, V, O and head strides; otherwise the element size) */
+} attn_status;
+
+/*
+ * attn_fwd - exact attention forward, one pass over all keys.
+ *   Q [B,H,N_q,d], K and V [B,H,N_kv,d] in `dtype`; O [B,H,N_q,d] in `dtype`; LSE [B,H,N_q] fp32.
+ *   causal: 0 or 1 (offset N_kv - N_q).  scale: any finite float (1/sqrt(d) is the usual choice).
+ * Source: "FlashAttention by hand", paragraphs on fused tiled attention, online softmax, the per-tile flow,
+ * rescaling and the single final division.
+ */
+int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+             int B, int H, int N_q, int N_kv, int d, int causal, float scale,
+             attn_dtype dtype, void* hip_stream);
+
+/*
+ * attn_fwd_ex - attn_fwd over a key range of a larger key/value tensor, with an explicit causal offset
+ * and output dtype.  This is one chunk of the chunked mode, and one device's step of a ring.
+ *   K, V            point at the first key of the range in head (0,0);
+ *   kv_head_stride  elements between consecutive (b,h) heads of K and V (0 means N_kv*d, contiguous);
+ *   causal_offset   key j of the range is visible to query i iff j <= i + causal_offset (when causal);
+ *   out_dtype       dtype of O: ATTN_F32 (partials to be merged) or the input dtype.
+ * Source: "Ring Attention with Blockwise Parallel Transformers" explainer, section 3 (blockwise
+ * computation over key/value blocks), and "FlashAttention by hand" as for attn_fwd.
+ */
+int attn_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                int B, int H, int N_q, int N_kv, int d, int causal, float scale,
+                long long causal_offset, long long kv_head_stride,
+                attn_dtype in_dtype, attn_dtype out_dtype, void* hip_stream);
+
+/*
+ * attn_merge - combine two partial results over disjoint key sets, row by row:
+ *     M = max(lse_a, lse_b);  w_x = exp(lse_x - M);  O = (w_a O_a + w_b O_b) / (w_a + w_b);
+ *     lse = M + ln(w_a + w_b);  rows with M = -inf give (0, -inf).
+ *   O_a, O_b [rows, d] in in_dtype; lse_a, lse_b, lse [rows] fp32; O [rows, d] in out_dtype.
+ *   In place is allowed when O == O_a (or O_b) and in_dtype == out_dtype, and lse == lse_a (or lse_b);
+ *   any other overlap is ATTN_ERR_BAD_ALIAS.  d >= 1.
+ * Source: "ATTENTION2D" explainer, sections 2 and 3 (partial statistics combined by commutativity and
+ * associativity); the rescale rule is the one of "FlashAttention by hand", paragraph on rescaling.
+ */
+int attn_merge(const void* O_a, const float* lse_a, const void* O_b, const float* lse_b,
+               void* O, float* lse, long long rows, int d,
+               attn_dtype in_dtype, attn_dtype out_dtype, void* hip_stream);
+
+/*
+ * attn_fwd_chunked_workspace_bytes - device workspace attn_fwd_chunked needs: two fp32 partial outputs
+ * [B,H,N_q,d] and two fp32 lse rows [B,H,N_q], each 256-byte aligned; 0 when P == 1.
+ * Returns 0 as well for invalid arguments (attn_fwd_chunked reports those).
+ */
+size_t attn_fwd_chunked_workspace_bytes(int B, int H, int N_q, int d, int P);
+
+/*
+ * attn_fwd_chunked - the keys are cut into P contiguous chunks, chunk p covering
+ * [floor(p*N_kv/P), floor((p+1)*N_kv/P)); each chunk is attended with attn_fwd_ex into fp32 partials and
+ * folded left to right with attn_merge; the last merge writes O in `dtype` and LSE.  Chunks that are
+ * empty or entirely in the causal future are skipped (they are the merge identity).  Result: equal to
+ * attn_fwd up to rounding.  P >= 1 (P > N_kv is allowed).  Everything is enqueued on one stream.
+ * Source: "Ring Attention with Blockwise Parallel Transformers" explainer, section 3 (key/value blocks
+ * visited one after another), and "ATTENTION2D" explainer, section 3 (staged combination).
+ */
+int attn_fwd_chunked(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                     int B, int H, int N_q, int N_kv, int d, int causal, float scale, int P,
+                     attn_dtype dtype, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* attn_strerror - a static string naming a status code. */
+const char* attn_strerror(int status);
+
+/* attn_last_error - a description of the last failure on the calling thread ("" if none). */
+const char* attn_last_error(void);
+
+/*
+ * Launch timing.  attn_timing_enable(1) makes every kernel launch of the library record a pair of HIP
+ * events on its stream (kind 0 = attention forward kernel, 1 = merge kernel); attn_timing_read
+ * synchronises those events, returns per-kind launch counts and summed durations in milliseconds, and
+ * clears the record.  attn_timing_enable(0) stops recording.  Used by the benchmark to time the kernels
+ * on the stream they run on; off by default.  Returns ATTN_ERR_HIP if an event call fails.
+ */
+int attn_timing_enable(int on);
+int attn_timing_read(long long counts[2], double total_ms[2]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

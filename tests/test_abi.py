@@ -1,0 +1,155 @@
+"""The C-ABI library on a host without a GPU: it loads, exports what include/attn.h declares, and rejects
+invalid arguments with the documented status before any HIP call (no call here reaches a kernel)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import exact_blockwise_attention_fwd_amd as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+# distinct, 256-byte aligned fake device addresses: never dereferenced, because validation fails first
+P = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(8)]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = A.lib()
+    names = declared_functions()
+    assert {"attn_fwd", "attn_fwd_ex", "attn_merge", "attn_fwd_chunked", "attn_fwd_chunked_workspace_bytes",
+            "attn_strerror", "attn_last_error", "attn_timing_enable", "attn_timing_read"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in attn.h but not exported"
+
+
+def test_status_codes_match_header():
+    text = open(HEADER).read()
+    codes = dict((name, int(v)) for name, v in re.findall(r"(ATTN_(?:OK|ERR_[A-Z_]+))\s*=\s*(\d+)", text))
+    assert codes == {v: k for k, v in A.STATUS.items()}
+    for name, code in codes.items():
+        s = A.lib().attn_strerror(code).decode()
+        assert s and s != "unknown status", name
+    assert A.lib().attn_strerror(99).decode() == "unknown status"
+
+
+def fwd(*, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=2, N_q=8, N_kv=8, d=64, causal=0, scale=0.125,
+        dtype=A.ATTN_BF16):
+    return A.lib().attn_fwd(q, k, v, o, lse, B, H, N_q, N_kv, d, causal, scale, dtype, None)
+
+
+def fwd_ex(*, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=2, N_q=8, N_kv=8, d=64, causal=0, scale=0.125,
+           offset=0, stride=0, din=A.ATTN_BF16, dout=A.ATTN_BF16):
+    return A.lib().attn_fwd_ex(q, k, v, o, lse, B, H, N_q, N_kv, d, causal, scale, offset, stride, din, dout, None)
+
+
+def merge(*, oa=P[0], la=P[1], ob=P[2], lb=P[3], o=P[4], lse=P[5], rows=16, d=64, din=A.ATTN_F32, dout=A.ATTN_F32):
+    return A.lib().attn_merge(oa, la, ob, lb, o, lse, rows, d, din, dout, None)
+
+
+def chunked(*, o=P[3], lse=P[4], P_=4, ws=P[6], ws_n=1 << 40, d=64, dtype=A.ATTN_BF16, N_q=8, N_kv=8):
+    return A.lib().attn_fwd_chunked(P[0], P[1], P[2], o, lse, 1, 2, N_q, N_kv, d, 0, 0.125, P_, dtype, ws, ws_n, None)
+
+
+def last_error():
+    return A.lib().attn_last_error().decode()
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_null_pointers(which):
+    assert fwd(**{which: None}) == 1 and "non-NULL" in last_error()
+    assert fwd_ex(**{which: None}) == 1
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N_q=0), dict(N_kv=0), dict(N_q=-3), dict(B=-1)])
+def test_bad_shapes(kw):
+    assert fwd(**kw) == 2
+
+
+def test_bad_kv_stride():
+    assert fwd_ex(stride=8 * 64 - 1) == 2      # smaller than N_kv*d
+
+
+@pytest.mark.parametrize("d,dtype", [(32, A.ATTN_BF16), (96, A.ATTN_BF16), (256, A.ATTN_BF16), (0, A.ATTN_F32),
+                                     (257, A.ATTN_F32)])
+def test_unsupported_head_dim(d, dtype):
+    assert fwd(d=d, dtype=dtype) == 3
+
+
+def test_bad_dtypes():
+    assert fwd(dtype=7) == 4
+    assert fwd_ex(din=A.ATTN_F32, dout=A.ATTN_BF16) == 4     # fp32 input cannot produce bf16 output
+    assert merge(din=3) == 4
+
+
+@pytest.mark.parametrize("scale", [math.nan, math.inf, -math.inf])
+def test_bad_scale(scale):
+    assert fwd(scale=scale) == 5
+
+
+def test_aliasing():
+    assert fwd(o=P[0]) == 7                     # O on top of Q
+    assert fwd(lse=P[2]) == 7                   # LSE on top of V
+    assert fwd(lse=P[3]) == 7                   # LSE on top of O
+    assert fwd(o=ctypes.c_void_p(P[1].value + 256)) == 7   # O inside K
+
+
+def test_misaligned():
+    assert fwd(q=ctypes.c_void_p(P[0].value + 8)) == 9      # bf16 needs 16-byte alignment
+    assert fwd(q=ctypes.c_void_p(P[0].value + 2), dtype=A.ATTN_F32) == 9
+    assert fwd_ex(stride=8 * 64 + 4) == 9       # bf16 head stride must keep 16-byte alignment
+
+
+def test_merge_validation():
+    assert merge(oa=None) == 1
+    assert merge(rows=0) == 2 and merge(d=0) == 2
+    assert merge(o=ctypes.c_void_p(P[0].value + 64)) == 7            # partial overlap with O_a
+    assert merge(o=P[0], din=A.ATTN_F32, dout=A.ATTN_BF16) == 7      # in place across dtypes
+    assert merge(lse=ctypes.c_void_p(P[1].value + 4)) == 7           # lse partially overlaps lse_a
+    assert merge(o=P[1]) == 7                                         # O over lse_a
+
+
+def test_chunked_validation():
+    need = A.lib().attn_fwd_chunked_workspace_bytes(1, 2, 8, 64, 4)
+    assert chunked(P_=0) == 2
+    assert chunked(ws=None) == 6
+    assert chunked(ws_n=need - 1) == 6
+    assert chunked(ws=ctypes.c_void_p(P[6].value + 16)) == 9
+    assert chunked(ws=P[1]) == 7                                      # workspace over K
+    assert chunked(d=100) == 3
+
+
+def test_workspace_formula():
+    f = A.lib().attn_fwd_chunked_workspace_bytes
+    assert f(1, 2, 8, 64, 1) == 0
+    rows = 1 * 32 * 16384
+    a256 = lambda x: (x + 255) // 256 * 256
+    assert f(1, 32, 16384, 128, 8) == 2 * a256(rows * 128 * 4) + 2 * a256(rows * 4)
+    assert f(1, 1, 3, 5, 2) == 2 * 256 + 2 * 256
+    assert f(0, 1, 1, 64, 2) == 0 and f(1, 1, 1, 64, 0) == 0
+
+
+def test_last_error_is_per_call():
+    assert fwd(scale=math.nan) == 5
+    assert "finite" in last_error()
+    assert fwd(d=48) == 3
+    assert "d = 64 or 128" in last_error()
+
+
+def test_timing_read_without_launches():
+    assert A.lib().attn_timing_enable(1) == 0
+    assert A.timing_read() == {"fwd": (0, 0.0), "merge": (0, 0.0)}
+    assert A.lib().attn_timing_enable(0) == 0
+
+
+def test_python_errors_name_the_status():
+    err = A.AttnError(3, "attn_fwd", "x")
+    assert "ATTN_ERR_UNSUPPORTED_D" in str(err) and err.status == 3

@@ -1,0 +1,276 @@
+"""GPU parity: the HIP path (called through the C ABI) against the fp64 CPU oracle, element by element.
+
+Small shapes are compared in full; they span several query and key tiles and end in ragged tails.  The five
+measured workloads run at full size in the launch configuration the bench times, and are compared on
+seeded query rows that the oracle evaluates one by one (64 per head).  Invariants that hold at any size
+(determinism, NaN-poisoned outputs overwritten, chunked = single pass) are checked on the GPU as well.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_blockwise_attention_fwd_amd as A
+import oracle
+import workloads as W
+from parity import assert_parity, errors, out_to_f64, storage_to_f64, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    A.lib()
+
+
+def make(w: W.Workload):
+    """Seeded storage arrays and device tensors for a workload."""
+    st = [W.tensor_storage(w, t) for t in (W.Q_T, W.K_T, W.V_T)]
+    return st, [to_device(s) for s in st]
+
+
+def oracle_full(st, w, chunks=1):
+    q, k, v = (storage_to_f64(s) for s in st)
+    return oracle.attention(q, k, v, w.scale, w.causal, w.offset, chunks=chunks)
+
+
+def rows_for(w: W.Workload, b: int, h: int, n: int = 64) -> np.ndarray:
+    if w.sample_rows:
+        return W.sample_rows(w, b, h)
+    rng = np.random.default_rng((w.seed, 77, b, h))
+    r = rng.choice(w.N_q, size=min(n, w.N_q), replace=False)
+    return np.unique(np.concatenate([r, [0, w.N_q - 1]]))
+
+
+def check_sampled(w, st, o_dev, lse_dev, heads=None, what=""):
+    """Compare sampled rows of every head (or the given heads) against the oracle's row-by-row result."""
+    o_all, l_all = [], []
+    ref_o, ref_l = [], []
+    for b in range(w.B):
+        for h in range(w.H):
+            if heads is not None and (b, h) not in heads:
+                continue
+            rows = rows_for(w, b, h)
+            q = storage_to_f64(st[0][b, h][rows])
+            k = storage_to_f64(st[1][b, h])
+            v = storage_to_f64(st[2][b, h])
+            o_r, l_r = oracle.naive_head(q, k, v, w.scale, w.causal, w.offset, rows)
+            idx = torch.from_numpy(rows).cuda()
+            o_all.append(out_to_f64(o_dev[b, h].index_select(0, idx)))
+            l_all.append(out_to_f64(lse_dev[b, h].index_select(0, idx)))
+            ref_o.append(o_r)
+            ref_l.append(l_r)
+    err = errors(np.concatenate(o_all), np.concatenate(l_all), np.concatenate(ref_o), np.concatenate(ref_l))
+    print(f"{what} {err}", flush=True)
+    assert_parity(err, w.dtype, what)
+    return err
+
+
+# ------------------------------------------------------------------------------ small shapes, full compare
+SMALL = [
+    # B, H, N_q, N_kv, d, causal, dtype
+    (1, 2, 300, 777, 128, False, "bf16"),
+    (1, 2, 300, 777, 128, True, "bf16"),
+    (2, 1, 333, 333, 128, True, "bf16"),
+    (1, 2, 257, 1000, 64, True, "bf16"),
+    (1, 2, 1000, 257, 64, True, "bf16"),    # N_q > N_kv: the first rows see no key
+    (1, 1, 1, 1, 128, False, "bf16"),
+    (1, 3, 5, 3, 64, False, "bf16"),
+    (1, 1, 129, 65, 64, False, "bf16"),
+    (1, 1, 640, 640, 128, True, "bf16"),
+    (1, 2, 200, 300, 64, False, "f32"),
+    (1, 2, 130, 70, 37, True, "f32"),
+    (1, 1, 64, 64, 256, True, "f32"),
+    (1, 1, 1, 5, 1, False, "f32"),
+    (2, 2, 100, 100, 128, True, "f32"),
+]
+
+
+def small_workload(i, case, q_std=1.0):
+    B, H, N_q, N_kv, d, causal, dt = case
+    return W.Workload(f"small{i}", B, H, N_q, N_kv, d, dt, causal, 1, seed=1000 + i, q_std=q_std)
+
+
+@pytest.mark.parametrize("i", range(len(SMALL)), ids=lambda i: "x".join(map(str, SMALL[i][:5])) +
+                         ("c" if SMALL[i][5] else "n") + SMALL[i][6])
+def test_small_full(i):
+    w = small_workload(i, SMALL[i])
+    st, (q, k, v) = make(w)
+    o_ref, l_ref = oracle_full(st, w)
+    o, lse = A.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    err = errors(out_to_f64(o), out_to_f64(lse), o_ref, l_ref)
+    print(w, err, flush=True)
+    assert_parity(err, w.dtype, w.name)
+    for P in sorted({2, 3, 7, w.N_kv + 2}):
+        o, lse = A.fwd_chunked(q, k, v, P, causal=w.causal, scale=w.scale)
+        torch.cuda.synchronize()
+        err = errors(out_to_f64(o), out_to_f64(lse), o_ref, l_ref)
+        assert_parity(err, w.dtype, f"{w.name} chunks={P}")
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_unusual_scales(scale, dt):
+    w = W.Workload("scales", 1, 2, 190, 260, 128 if dt == "bf16" else 64, dt, True, 1, seed=2000)
+    st, (q, k, v) = make(w)
+    qq, kk, vv = (storage_to_f64(s) for s in st)
+    o_ref, l_ref = oracle.attention(qq, kk, vv, scale, True, w.offset)
+    o, lse = A.fwd(q, k, v, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    assert_parity(errors(out_to_f64(o), out_to_f64(lse), o_ref, l_ref), dt, f"scale={scale}")
+
+
+def test_peaky_sorted_keys_rescale_every_tile():
+    """Keys sorted by ascending logit for query 0: its running max rises on every key tile."""
+    w = W.Workload("sorted", 1, 1, 256, 2048, 128, "bf16", False, 1, seed=2100, q_std=4.0)
+    st, _ = make(w)
+    q64 = storage_to_f64(st[0][0, 0])
+    order = np.argsort(storage_to_f64(st[1][0, 0]) @ q64[0])
+    st[1] = st[1][:, :, order].copy()
+    st[2] = st[2][:, :, order].copy()
+    q, k, v = (to_device(s) for s in st)
+    o_ref, l_ref = oracle_full(st, w)
+    o, lse = A.fwd(q, k, v, causal=False, scale=w.scale)
+    torch.cuda.synchronize()
+    assert_parity(errors(out_to_f64(o), out_to_f64(lse), o_ref, l_ref), "bf16", "sorted keys")
+
+
+def test_key_range_and_offset_partials():
+    """attn_fwd_ex over two key ranges (fp32 partials with explicit offsets) merged = the whole."""
+    w = W.Workload("ranges", 1, 2, 384, 1000, 128, "bf16", True, 1, seed=2200)
+    st, (q, k, v) = make(w)
+    o_ref, l_ref = oracle_full(st, w)
+    cut = 437
+    off = w.N_kv - w.N_q
+    oa, la = A.fwd_ex(q, k, v, True, w.scale, causal_offset=off, key_range=(0, cut), out_dtype=torch.float32)
+    ob, lb = A.fwd_ex(q, k, v, True, w.scale, causal_offset=off - cut, key_range=(cut, w.N_kv),
+                      out_dtype=torch.float32)
+    o, lse = A.merge(oa, la, ob, lb, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert_parity(errors(out_to_f64(o), out_to_f64(lse), o_ref, l_ref), "bf16", "two ranges merged")
+    # the fp32 partials themselves against the oracle's partials
+    qq, kk, vv = (storage_to_f64(s) for s in st)
+    pa = oracle.attention(qq, kk[:, :, :cut], vv[:, :, :cut], w.scale, True, off)
+    err = errors(out_to_f64(oa), out_to_f64(la), *pa)
+    assert_parity(err, "bf16", "partial a")
+
+
+# ------------------------------------------------------------------------------------------------- merge
+@pytest.mark.parametrize("din,dout,d", [("f32", "f32", 128), ("f32", "bf16", 128), ("bf16", "bf16", 64),
+                                        ("f32", "f32", 37), ("bf16", "f32", 5)])
+def test_merge_vs_oracle(din, dout, d):
+    rng = np.random.default_rng(3000 + d)
+    rows = 3001
+    oa, ob = rng.standard_normal((rows, d)).astype(np.float32), rng.standard_normal((rows, d)).astype(np.float32)
+    la, lb = (rng.standard_normal(rows) * 5).astype(np.float32), (rng.standard_normal(rows) * 5).astype(np.float32)
+    la[::7] = -np.inf
+    lb[::11] = -np.inf
+    oa[::7] = 0
+    ob[::11] = 0
+    if din == "bf16":
+        oa, ob = W.f32_to_bf16_bits(oa), W.f32_to_bf16_bits(ob)
+    ref_o, ref_l = oracle.merge(storage_to_f64(oa), la.astype(np.float64), storage_to_f64(ob), lb.astype(np.float64))
+    tdt = torch.bfloat16 if dout == "bf16" else torch.float32
+    o, lse = A.merge(to_device(oa), to_device(la), to_device(ob), to_device(lb), out_dtype=tdt)
+    torch.cuda.synchronize()
+    err = errors(out_to_f64(o), out_to_f64(lse), ref_o, ref_l)
+    tol = 2e-2 if dout == "bf16" else 1e-5
+    assert not err["nan"] and err["lse_inf_match"]
+    assert err["max_abs"] <= tol and err["lse_abs"] <= 1e-5, err
+
+
+def test_merge_in_place():
+    rng = np.random.default_rng(3100)
+    rows, d = 4096, 128
+    oa, ob = rng.standard_normal((rows, d)).astype(np.float32), rng.standard_normal((rows, d)).astype(np.float32)
+    la, lb = rng.standard_normal(rows).astype(np.float32), rng.standard_normal(rows).astype(np.float32)
+    ref_o, ref_l = oracle.merge(oa, la, ob, lb)
+    ta, tla = to_device(oa), to_device(la)
+    o, lse = A.merge(ta, tla, to_device(ob), to_device(lb), out=ta, lse=tla)
+    torch.cuda.synchronize()
+    assert o.data_ptr() == ta.data_ptr()
+    err = errors(out_to_f64(ta), out_to_f64(tla), ref_o, ref_l)
+    assert err["max_abs"] <= 1e-5 and err["lse_abs"] <= 1e-5, err
+
+
+# --------------------------------------------------------------------------- invariants on the GPU itself
+def test_determinism_and_poisoned_outputs():
+    w = W.Workload("det", 2, 4, 1500, 1500, 128, "bf16", True, 1, seed=4000)
+    st, (q, k, v) = make(w)
+    o1 = torch.full_like(q, float("nan"))
+    l1 = torch.full((2, 4, 1500), float("nan"), device="cuda")
+    A.fwd(q, k, v, causal=True, out=o1, lse=l1)
+    o2, l2 = A.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o1).any() and not torch.isnan(l1).any()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_constant_v_gives_constant_output():
+    w = W.Workload("ones", 1, 2, 700, 900, 128, "bf16", True, 1, seed=4100)
+    st, (q, k, v) = make(w)
+    o, lse = A.fwd(q, k, torch.ones_like(v), causal=True)
+    torch.cuda.synchronize()
+    assert (o.float() - 1).abs().max().item() <= 2e-2
+
+
+# -------------------------------------------------------------------------- the measured workloads, full size
+def test_tiny_fp32_full_and_4_chunks():
+    w = W.WORKLOADS["tiny_fp32"]
+    st, (q, k, v) = make(w)
+    o_ref, l_ref = oracle_full(st, w)
+    o, lse = A.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    oc, lc = A.fwd_chunked(q, k, v, w.chunks, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert_parity(errors(out_to_f64(o), out_to_f64(lse), o_ref, l_ref), "f32", "tiny single pass")
+    assert_parity(errors(out_to_f64(oc), out_to_f64(lc), o_ref, l_ref), "f32", "tiny 4 chunks")
+
+
+def test_causal_prefill_4k():
+    w = W.WORKLOADS["causal_prefill_4k"]
+    st, (q, k, v) = make(w)
+    o, lse = A.fwd(q, k, v, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    check_sampled(w, st, o, lse, what="causal_prefill_4k sampled")
+    # two heads in full
+    for b, h in [(0, 0), (3, 15)]:
+        sub = [s[b:b + 1, h:h + 1] for s in st]
+        o_ref, l_ref = oracle_full(sub, w)
+        err = errors(out_to_f64(o[b:b + 1, h:h + 1]), out_to_f64(lse[b:b + 1, h:h + 1]), o_ref, l_ref)
+        assert_parity(err, "bf16", f"causal_prefill_4k head ({b},{h}) full")
+
+
+def test_peaky_16k():
+    w = W.WORKLOADS["peaky_16k"]
+    st, (q, k, v) = make(w)
+    o, lse = A.fwd(q, k, v, causal=False, scale=w.scale)
+    torch.cuda.synchronize()
+    check_sampled(w, st, o, lse, what="peaky_16k sampled")
+
+
+def test_ring_share_128k_chunked():
+    w = W.WORKLOADS["ring_share_128k"]
+    st, (q, k, v) = make(w)
+    o, lse = A.fwd_chunked(q, k, v, w.chunks, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    check_sampled(w, st, o, lse, what="ring_share_128k 8 chunks sampled")
+    o1, l1 = A.fwd(q, k, v, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    check_sampled(w, st, o1, l1, heads={(0, 0), (0, 31)}, what="ring_share_128k single pass sampled")
+    # chunked = single pass at any size (GPU against GPU)
+    assert (o.float() - o1.float()).abs().max().item() <= 2e-2
+    assert (lse - l1).abs().max().item() <= 1e-4
+
+
+def test_ulysses_share_256k():
+    w = W.WORKLOADS["ulysses_share_256k"]
+    st, (q, k, v) = make(w)
+    o, lse = A.fwd(q, k, v, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    check_sampled(w, st, o, lse, what="ulysses_share_256k seeded rows")
