@@ -194,16 +194,19 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void fwd_bf16_kernel(FwdArgs a
     const int wave_full_end = CAUSAL ? min(a.n_kv, qw0 + a.offset + 1) : a.n_kv;      // keys < this: all visible
 
     // Q^T fragments (B operand): query qi, head-dim elements 16*ks + 8*h .. +7
+    // A negative scale negates Q (exact in bf16) so that every exponent is taken against a running max;
+    // a zero scale zeroes Q, which gives the same all-zero logits without multiplying -inf by zero.
     const float scale_abs = fabsf(a.scale);
-    const unsigned neg = a.scale < 0.f ? 0x80008000u : 0u;   // negating bf16 Q is exact
+    const unsigned neg = a.scale < 0.f ? 0x80008000u : 0u;
+    const unsigned keep = a.scale == 0.f ? 0u : 0xffffffffu;
     bf16x8 qf[T::NKS];
 #pragma unroll
     for (int ks = 0; ks < T::NKS; ++ks) {
         u32x4 x = q_ok ? *reinterpret_cast<const u32x4*>(qh + (size_t)qi * D + 16 * ks + 8 * h) : u32x4{0, 0, 0, 0};
-        x ^= neg;
+        x = (x ^ neg) & keep;
         qf[ks] = as_bf16x8(x);
     }
-    const float c = scale_abs * LOG2E;
+    const float c = a.scale == 0.f ? LOG2E : scale_abs * LOG2E;   // scale * log2(e), always > 0
 
     f32x16 acc[T::NDB];
 #pragma unroll
@@ -261,7 +264,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void fwd_bf16_kernel(FwdArgs a
             const float mc = m_use * c;
             // ---- rescale what was accumulated under the old max (skipped when no max moved: alpha == 1)
             const float alpha = __builtin_amdgcn_exp2f(m * c - mc);
-            if (__builtin_amdgcn_read_exec() && __any(m_new > m)) {
+            if (__any(m_new > m)) {
 #pragma unroll
                 for (int db = 0; db < T::NDB; ++db) acc[db] *= alpha;
                 l *= alpha;

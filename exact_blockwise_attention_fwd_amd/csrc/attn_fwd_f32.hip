@@ -3,9 +3,11 @@
 // Same algorithm as the bf16 kernel ("FlashAttention by hand": key/value tiles streamed through on-chip
 // memory, running max, running denominator, rescale on a new max, one final division), written for
 // exactness rather than speed: no fp32 matrix cores (gfx950 has no xf32 MFMA and the fp32 path only serves
-// small problems), accurate expf/logf, and scores computed in fp32 with the scale applied to the dot
-// product.  A workgroup owns 64 query rows; four lanes share a row, each holding a quarter of the head
-// dimension in float4 chunks, and K/V tiles of 32 keys are staged in LDS with zero padding.
+// small problems) and accurate expf/logf.  Dot products, scaled logits and the running max are kept in
+// fp64, so that the rounding of an fp32 dot product (which grows with the logit magnitude) does not reach
+// the softmax weights; weights, the denominator and the output accumulate in fp32.  A workgroup owns 64
+// query rows; four lanes share a row, each holding a quarter of the head dimension in float4 chunks, and
+// K/V tiles of 32 keys are staged in LDS with zero padding.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -54,7 +56,8 @@ __global__ __launch_bounds__(F_THREADS) void fwd_f32_kernel(FwdArgs a, int num_q
     const int kv_end = a.causal ? max(0, min(a.n_kv, q_last + a.offset + 1)) : a.n_kv;
     const int lim = a.causal ? min(a.n_kv - 1, qi + a.offset) : a.n_kv - 1;   // last key visible to qi
 
-    float m = -INFINITY, l = 0.f;
+    double m = -INFINITY;
+    float l = 0.f;
     for (int kt = 0; kt < kv_end; kt += F_TKV) {
         __syncthreads();
         for (int idx = tid; idx < F_TKV * DMAX; idx += F_THREADS) {
@@ -65,33 +68,33 @@ __global__ __launch_bounds__(F_THREADS) void fwd_f32_kernel(FwdArgs a, int num_q
         }
         __syncthreads();
 
-        float s[F_TKV];
-        float mt = -INFINITY;
+        double s[F_TKV];
+        double mt = -INFINITY;
 #pragma unroll
         for (int j = 0; j < F_TKV; ++j) {
-            float part = 0.f;
+            double part = 0.0;
 #pragma unroll
             for (int i = 0; i < NCH; ++i) {
                 const f32x4 k4 = ks[j][4 * i + r];
-                part = fmaf(q[i][0], k4[0], part);
-                part = fmaf(q[i][1], k4[1], part);
-                part = fmaf(q[i][2], k4[2], part);
-                part = fmaf(q[i][3], k4[3], part);
+                part = fma((double)q[i][0], (double)k4[0], part);
+                part = fma((double)q[i][1], (double)k4[1], part);
+                part = fma((double)q[i][2], (double)k4[2], part);
+                part = fma((double)q[i][3], (double)k4[3], part);
             }
             part += __shfl_xor(part, 1, 64);
             part += __shfl_xor(part, 2, 64);
-            s[j] = (kt + j <= lim) ? part * a.scale : -INFINITY;
-            mt = fmaxf(mt, s[j]);
+            s[j] = (kt + j <= lim) ? part * (double)a.scale : -INFINITY;
+            mt = fmax(mt, s[j]);
         }
-        const float m_new = fmaxf(m, mt);
+        const double m_new = fmax(m, mt);
         if (m_new == -INFINITY) continue;        // nothing visible yet for this row
-        const float alpha = m == -INFINITY ? 0.f : expf(m - m_new);
+        const float alpha = m == -INFINITY ? 0.f : expf((float)(m - m_new));
         l *= alpha;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) acc[i] *= alpha;
 #pragma unroll
         for (int j = 0; j < F_TKV; ++j) {
-            const float p = expf(s[j] - m_new);   // exp(-inf) = 0 for masked keys
+            const float p = expf((float)(s[j] - m_new));   // exp(-inf) = 0 for masked keys
             l += p;
 #pragma unroll
             for (int i = 0; i < NCH; ++i) {
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(F_THREADS) void fwd_f32_kernel(FwdArgs a, int num_q
             const int cc = 16 * i + 4 * r + e;
             if (cc < d) oh[cc] = acc[i][e] * inv;
         }
-    if (r == 0) a.lse[(size_t)bh * a.n_q + qi] = l > 0.f ? m + logf(l) : -INFINITY;
+    if (r == 0) a.lse[(size_t)bh * a.n_q + qi] = l > 0.f ? (float)(m + (double)logf(l)) : -INFINITY;
 }
 
 template <int DMAX>
