@@ -96,6 +96,9 @@ def main():
     ap.add_argument("--workload", default="ring_share_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="time a plain 1 GiB device-to-device copy instead (practical HBM ceiling; also the "
+                         "reference size for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path is one device's share); --gpus {args.gpus} is not "
@@ -110,6 +113,22 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        c1.record()
+        torch.cuda.synchronize()
+        ms = c0.elapsed_time(c1) / args.steps
+        print(json.dumps({"copy_bytes": n, "ms_per_copy": ms, "gbs_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}))
+        return
     A.lib()
     w = W.WORKLOADS[args.workload]
     log(f"workload {w}")

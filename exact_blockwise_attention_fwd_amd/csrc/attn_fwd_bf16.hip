@@ -14,23 +14,34 @@
 //    reductions plus one exchange between the two half-waves, and the per-query rescale factor is a
 //    per-lane scalar.
 //  * The A rows of S^T are read from K with bits 2 and 3 of the row index swapped.  That puts keys
-//    16*(j/8) + 8*(l/32) + (j%8) into accumulator element j of lane l, so the fp32 scores of one
-//    16-key k-step are 8 consecutive keys per lane: exactly the B operand (P^T) that the P.V MFMA needs,
-//    with no cross-lane shuffle, and the matching A operand (V^T) is one 16-byte LDS read.
-//  * O^T = V^T P^T accumulates in 32x32 blocks over d; V is transposed while it is staged into LDS
-//    (byte permutes in registers, 8-byte LDS writes).
-//  * K/V tiles are double-buffered in LDS: the global loads of tile t+1 are in flight while tile t is
-//    computed; one workgroup barrier per tile.
-//  * LDS rows are XOR-swizzled in 16-byte units so that the MFMA operand reads of 16 consecutive lanes hit
-//    distinct banks.
-//  * exp is v_exp_f32 (base 2) with scale*log2(e) folded into one FMA per score; the rescale of the
-//    output accumulator is skipped, exactly, when no row max of the wave moved.
+//    16*(j/8) + 8*(l/32) + (j%8) into accumulator element j of lane l, so the fp32 scores of one 16-key
+//    k-step are 8 consecutive keys per lane: exactly the B operand (P^T) that the P.V MFMA needs, with no
+//    cross-lane shuffle.
+//  * O^T = V^T P^T accumulates in 32x32 blocks over d.  Its A operand (V^T: one head-dim row, 8 keys per
+//    lane) comes straight from the row-major V tile through ds_read_b64_tr_b16, the LDS transpose read:
+//    within each 16-lane block, lane 4e+s points at 4 head-dim values of key e and lane i receives head-dim
+//    value i of keys 0..3, so two such reads give a lane its 8 keys.
+//  * K and V tiles move from HBM to LDS with buffer_load_dwordx4 ... lds: no staging registers, no LDS
+//    store instructions, and loads past the last key return zeros (the buffer resource's bound).  Each
+//    wave instruction fills one contiguous 1 KiB LDS segment in lane order, so the XOR swizzle of the LDS
+//    layout is applied by choosing which 16-byte global chunk each lane fetches.
+//  * Tiles are double-buffered: the loads of tile t+2 are issued right after the barrier that retires tile
+//    t, and land while tile t+1 is computed; one workgroup barrier per tile.
+//  * LDS rows are XOR-swizzled in 16-byte units so that the operand reads of each 16-lane block (K rows for
+//    S^T, four V rows for the transpose read) hit distinct banks.
+//  * exp is v_exp_f32 (base 2) with scale*log2(e) folded into one FMA per score.  The running max used as
+//    the exponent reference is only moved when some row of the wave has grown by more than 2^8 (in exp2
+//    units); until then the stale reference bounds every weight by 2^8, which fp32 sums and bf16 weights
+//    carry without loss, and the final division by the denominator accumulated against the same reference
+//    returns the same result.  Rescaling the output accumulator therefore becomes rare.
 //  * Workgroup ids are remapped so that consecutive logical tiles (same head, neighbouring query rows,
 //    hence the same K/V stream) land on the same XCD and share its L2; causal launches start with the
 //    longest query tiles.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "attn_internal.h"
 
@@ -43,56 +54,52 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float RESCALE_SLACK = 8.0f;   // exp2 units the exponent reference may lag the running max
 constexpr int NXCD = 8;
+constexpr unsigned BUF_RSRC_WORD3 = 0x00020000u;   // raw buffer, 32-bit data format, bounds-checked
 
 template <int D>
 struct Tile {
-    static constexpr int NW = 4;                 // waves per workgroup
+    static constexpr int NW = 4;                     // waves per workgroup
     static constexpr int THREADS = 64 * NW;
-    static constexpr int BR = 32 * NW;           // query rows per workgroup
-    static constexpr int BC = D == 128 ? 64 : 128;  // keys per tile
-    static constexpr int NKB = BC / 32;          // 32-key blocks of S^T per tile
-    static constexpr int NDB = D / 32;           // 32-row blocks of O^T
-    static constexpr int NKS = D / 16;           // k-steps of S^T (over d)
-    static constexpr int KROW = 2 * D;           // bytes per K row in LDS
-    static constexpr int VROW = 2 * BC;          // bytes per V^T row in LDS
-    static constexpr int KBYTES = BC * KROW;
-    static constexpr int VBYTES = D * VROW;
-    static constexpr int BUF = KBYTES + VBYTES;
-    static constexpr int LDS = 2 * BUF;
-    static constexpr int KCH = D / 8;            // 16-byte chunks per K row
-    static constexpr int VCH = BC / 8;           // 16-byte chunks per V^T row
-    static constexpr int K_LOADS = BC * KCH / THREADS;   // 16-byte K loads per thread per tile
-    static_assert(BC * KCH % THREADS == 0, "K tile split");
-    static_assert((BC / 4) * (D / 8) == THREADS, "V tile split: one 4-key x 8-d block per thread");
+    static constexpr int BR = 32 * NW;               // query rows per workgroup
+    static constexpr int BC = D == 128 ? 64 : 128;   // keys per tile
+    static constexpr int NKB = BC / 32;              // 32-key blocks of S^T per tile
+    static constexpr int NDB = D / 32;               // 32-row blocks of O^T
+    static constexpr int NKS = D / 16;               // k-steps of S^T (over d)
+    static constexpr int ROW = 2 * D;                // bytes per K or V row in LDS
+    static constexpr int TILE = BC * ROW;            // bytes of one K (or V) tile
+    static constexpr int SEGS = TILE / 1024;         // 1 KiB load segments per tile
+    static constexpr int SEGS_PER_WAVE = SEGS / NW;
+    static constexpr int RPS = 1024 / ROW;           // rows per segment
+    static constexpr int LPR = ROW / 16;             // lanes (16-byte chunks) per row
+    static constexpr int LDS = 5 * TILE;             // K double-buffered, then V triple-buffered
+    static_assert(SEGS % NW == 0, "segments split evenly over the waves");
+    static_assert(TILE == 16384, "both configurations use 16 KiB tiles");
 };
 
-// bits 2 and 3 of a key slot swapped (an involution)
+// bits 2 and 3 of a row index swapped (an involution)
 __device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
-// byte offset of 16-byte chunk c of K row r inside a K tile
+// XOR applied to the 16-byte chunk index of K row r.  Read side: lane slot rho = swap23(r & 15) reads it.
 template <int D>
-__device__ __forceinline__ int k_off(int r, int c) {
+__device__ __forceinline__ int k_swz(int r) {
     const int rho = swap23(r & 15);
-    int phys;
-    if constexpr (D == 128) phys = c ^ (rho & 15);
-    else phys = c ^ ((rho & 7) ^ ((rho >> 3) & 1));
-    return r * Tile<D>::KROW + phys * 16;
+    if constexpr (D == 128) return rho & 15;
+    else return (rho & 7) ^ ((rho >> 3) & 1);
 }
 
-// byte offset of 16-byte chunk c (8 keys) of V^T row dd (head-dim index) inside a V^T tile
+// XOR applied to the 16-byte chunk index of V row (key) r, chosen for the transpose reads
 template <int D>
-__device__ __forceinline__ int v_off(int dd, int c) {
-    int phys;
-    if constexpr (Tile<D>::VCH == 8) phys = c ^ ((dd ^ (dd >> 3)) & 7);
-    else phys = c ^ (dd & 15);
-    return dd * Tile<D>::VROW + phys * 16;
-}
-
-__device__ __forceinline__ u32x4 lds_read16(const char* base, int off) {
-    return *reinterpret_cast<const u32x4*>(base + off);
+__device__ __forceinline__ int v_swz(int r) {
+    if constexpr (D == 128) return 4 * (r & 3);
+    else return 4 * ((r >> 1) & 1);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -104,60 +111,11 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
-template <int D>
-struct Staged {            // one tile's global loads held in registers until written to LDS
-    u32x4 k[Tile<D>::K_LOADS];
-    u32x4 v[4];
-};
-
-template <int D>
-__device__ __forceinline__ void load_tile(Staged<D>& st, const uint16_t* kh, const uint16_t* vh, int kt,
-                                          int n_kv, int tid) {
-    using T = Tile<D>;
-#pragma unroll
-    for (int i = 0; i < T::K_LOADS; ++i) {
-        const int q = tid + T::THREADS * i;
-        const int r = q / T::KCH, c = q % T::KCH;
-        const int key = kt + r;
-        st.k[i] = key < n_kv ? *reinterpret_cast<const u32x4*>(kh + (size_t)key * D + c * 8) : u32x4{0, 0, 0, 0};
-    }
-    const int kg = tid / (D / 8), dc = tid % (D / 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int key = kt + 4 * kg + i;
-        st.v[i] = key < n_kv ? *reinterpret_cast<const u32x4*>(vh + (size_t)key * D + dc * 8) : u32x4{0, 0, 0, 0};
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void store_tile(const Staged<D>& st, char* buf, int tid) {
-    using T = Tile<D>;
-#pragma unroll
-    for (int i = 0; i < T::K_LOADS; ++i) {
-        const int q = tid + T::THREADS * i;
-        const int r = q / T::KCH, c = q % T::KCH;
-        *reinterpret_cast<u32x4*>(buf + k_off<D>(r, c)) = st.k[i];
-    }
-    // transpose a 4-key x 8-d block: for head-dim element e, the four keys' values become one 8-byte unit
-    const int kg = tid / (D / 8), dc = tid % (D / 8);
-    char* vt = buf + T::KBYTES;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {           // dword w holds head-dim elements 2w, 2w+1
-        const unsigned lo_e = __builtin_amdgcn_perm(st.v[1][w], st.v[0][w], 0x05040100u);
-        const unsigned hi_e = __builtin_amdgcn_perm(st.v[3][w], st.v[2][w], 0x05040100u);
-        const unsigned lo_o = __builtin_amdgcn_perm(st.v[1][w], st.v[0][w], 0x07060302u);
-        const unsigned hi_o = __builtin_amdgcn_perm(st.v[3][w], st.v[2][w], 0x07060302u);
-        const int d0 = 8 * dc + 2 * w;
-        *reinterpret_cast<u32x2*>(vt + v_off<D>(d0, kg >> 1) + 8 * (kg & 1)) = u32x2{lo_e, hi_e};
-        *reinterpret_cast<u32x2*>(vt + v_off<D>(d0 + 1, kg >> 1) + 8 * (kg & 1)) = u32x2{lo_o, hi_o};
-    }
-}
-
 template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(Tile<D>::THREADS, 2) void fwd_bf16_kernel(FwdArgs a, int num_qt, int total,
                                                                       int per_xcd) {
     using T = Tile<D>;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     // XCD-aware remap: hardware workgroup w runs on XCD w % 8; give each XCD a contiguous logical range
     const int w_hw = blockIdx.x;
@@ -169,7 +127,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void fwd_bf16_kernel(FwdArgs a
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;                         // half-wave
     const int col = lane & 31;                       // query slot within the wave
 
@@ -188,12 +146,43 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void fwd_bf16_kernel(FwdArgs a
     if (CAUSAL) kv_end = max(0, min(a.n_kv, q_last + a.offset + 1));
     const int ntiles = (kv_end + T::BC - 1) / T::BC;
 
-    // per-wave visibility bounds
+    // per-wave visibility bounds (wave-uniform)
     const int qw_last = min(qw0 + 31, a.n_q - 1);
-    const int wave_key_end = CAUSAL ? min(kv_end, qw_last + a.offset + 1) : kv_end;   // exclusive
+    const int wave_key_end = qw0 >= a.n_q ? 0 : CAUSAL ? min(kv_end, qw_last + a.offset + 1) : kv_end;   // exclusive
     const int wave_full_end = CAUSAL ? min(a.n_kv, qw0 + a.offset + 1) : a.n_kv;      // keys < this: all visible
 
-    // Q^T fragments (B operand): query qi, head-dim elements 16*ks + 8*h .. +7
+    // ---- global -> LDS loads.  Each tile gets buffer resources whose base is the tile's first key and whose
+    // bound is the rest of this head's key range, so loads past the last key return zeros; the whole
+    // offset is in the per-lane VGPR offset (the scalar offset stays 0).
+    const long long kv_bytes = (long long)a.n_kv * T::ROW;
+    // this wave fills segments wave, wave+NW, ...; lane L writes row RPS*seg + L/LPR, physical chunk L%LPR.
+    // Rows of segment wave+NW*k are those of segment `wave` plus NW*RPS*k (= 4096*k bytes), and the
+    // swizzles only look at row bits that this shift leaves alone.
+    int k_voff, v_voff;
+    {
+        const int r0 = T::RPS * wave + lane / T::LPR;
+        const int p = lane % T::LPR;
+        k_voff = r0 * T::ROW + 16 * (p ^ k_swz<D>(r0));
+        v_voff = r0 * T::ROW + 16 * (p ^ v_swz<D>(r0));
+    }
+    auto issue_tile = [&](int t) {
+        char* kbuf = smem + (t & 1) * T::TILE;
+        char* vbuf = smem + 2 * T::TILE + (t % 3) * T::TILE;
+        const long long base = (long long)t * T::TILE;
+        const int left = (int)(kv_bytes - base);
+        const __amdgpu_buffer_rsrc_t krs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)kh + base), (short)0, left, BUF_RSRC_WORD3);
+        const __amdgpu_buffer_rsrc_t vrs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)vh + base), (short)0, left, BUF_RSRC_WORD3);
+#pragma unroll
+        for (int k = 0; k < T::SEGS_PER_WAVE; ++k) {
+            const int seg = wave + T::NW * k;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kbuf + seg * 1024), 16, k_voff + 4096 * k, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vbuf + seg * 1024), 16, v_voff + 4096 * k, 0, 0, 0);
+        }
+    };
+
+    // ---- Q^T fragments (B operand): query qi, head-dim elements 16*ks + 8*h .. +7.
     // A negative scale negates Q (exact in bf16) so that every exponent is taken against a running max;
     // a zero scale zeroes Q, which gives the same all-zero logits without multiplying -inf by zero.
     const float scale_abs = fabsf(a.scale);
@@ -208,41 +197,62 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void fwd_bf16_kernel(FwdArgs a
     }
     const float c = a.scale == 0.f ? LOG2E : scale_abs * LOG2E;   // scale * log2(e), always > 0
 
+    // ---- per-lane LDS read offsets (the tile buffer and (kb, ks) parts are added as immediates)
+    const int kslot = swap23(col);                   // K row (within a 32-key block) feeding A-row `col`
+    int k_roff[T::NKS];
+#pragma unroll
+    for (int ks = 0; ks < T::NKS; ++ks) k_roff[ks] = kslot * T::ROW + 16 * ((2 * ks + h) ^ k_swz<D>(kslot));
+    // transpose reads: block b = lane/16 -> half-wave h and head-dim half dp; e = key within a group of
+    // four, s4 = which 4 head-dim values of the 16
+    int v_roff[T::NDB];
+    {
+        const int b = lane >> 4, j = lane & 15, e = j >> 2, s4 = j & 3, dp = b & 1;
+#pragma unroll
+        for (int db = 0; db < T::NDB; ++db) {
+            const int chunk = 4 * db + 2 * dp + (s4 >> 1);
+            v_roff[db] = (8 * h + e) * T::ROW + 16 * (chunk ^ v_swz<D>(e)) + 8 * (s4 & 1);
+        }
+    }
+
     f32x16 acc[T::NDB];
 #pragma unroll
     for (int db = 0; db < T::NDB; ++db) acc[db] = f32x16{};
-    float m = -INFINITY;   // running max of the raw dot products of this lane's query
-    float l = 0.f;         // running denominator, this half-wave's keys only
+    float m = -INFINITY;   // exponent reference: running max of this query's raw dot products (may lag)
+    float l = 0.f;         // running denominator against m, this half-wave's keys only
+    u32x4 p_cur[T::NKB][2];   // bf16 weights of the previous tile, consumed by its P.V one iteration later
 
-    Staged<D> st;
-    if (ntiles > 0) {
-        load_tile<D>(st, kh, vh, 0, a.n_kv, tid);
-        store_tile<D>(st, smem, tid);
-        if (ntiles > 1) load_tile<D>(st, kh, vh, T::BC, a.n_kv, tid);
-    }
-    __syncthreads();
+    // Tiles this wave computes: a prefix [0, wave_tiles) of the workgroup's ntiles (causal waves stop early).
+    const int wave_tiles = min(ntiles, (wave_key_end + T::BC - 1) / T::BC);
 
-    const int kslot = swap23(col);   // K row (within a 32-key block) that feeds A-row `col`
-
-    for (int t = 0; t < ntiles; ++t) {
-        const char* buf = smem + (t & 1) * T::BUF;
-        const int kt = t * T::BC;
-        if (kt < wave_key_end) {
-            // ---- S^T = K Q^T for BC keys x 32 queries
-            f32x16 s[T::NKB];
+    // One pipelined step at tile t: S(t) = K_t Q^T, the new exponent reference, the weights of tile t, and
+    // the P.V product of tile t-1 (weights from the previous step).  The weights of tile t and the P.V
+    // MFMAs of tile t-1 are independent and sit in one straight-line block, so the compiler can issue the
+    // softmax instructions while the matrix cores run.  An output rescale caused by tile t is applied at
+    // the start of the next step, i.e. after P.V(t-1) (old reference) and before P.V(t) (new reference).
+    float alpha_prev = 1.f;
+    bool moved_prev = false;
+    auto step = [&](auto do_s, auto do_pv, bool masked, int t, const char* __restrict__ kbuf,
+                    const char* __restrict__ vbuf) {
+        constexpr bool DO_S = decltype(do_s)::value, DO_PV = decltype(do_pv)::value;
+        if (moved_prev) {
+#pragma unroll
+            for (int db = 0; db < T::NDB; ++db) acc[db] *= alpha_prev;
+        }
+        f32x16 s[T::NKB];
+        u32x4 p_next[T::NKB][2];
+        if constexpr (DO_S) {
+            const int kt = t * T::BC;
 #pragma unroll
             for (int kb = 0; kb < T::NKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < T::NKS; ++ks) {
 #pragma unroll
                 for (int kb = 0; kb < T::NKB; ++kb) {
-                    const bf16x8 kf = as_bf16x8(lds_read16(buf, k_off<D>(32 * kb + kslot, 2 * ks + h)));
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb], 0, 0, 0);
+                    const u32x4 kv = *reinterpret_cast<const u32x4*>(kbuf + k_roff[ks] + 32 * kb * T::ROW);
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qf[ks], s[kb], 0, 0, 0);
                 }
             }
-            // ---- mask keys past the end or in the causal future (diagonal / ragged tiles only)
-            const bool need_mask = (kt + T::BC > wave_full_end) || (kt + T::BC > a.n_kv);
-            if (need_mask) {
+            if (masked) {   // keys past the end or in the causal future
                 const int lim = CAUSAL ? min(a.n_kv - 1, qi + a.offset) : a.n_kv - 1;   // last visible key
 #pragma unroll
                 for (int kb = 0; kb < T::NKB; ++kb)
@@ -252,26 +262,18 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void fwd_bf16_kernel(FwdArgs a
                         if (key > lim) s[kb][j] = -INFINITY;
                     }
             }
-            // ---- running max
+            // tile max; the reference moves (for every row of the wave) only when some row outgrew it
             float mt = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) mt = fmaxf(mt, s[kb][j]);
             mt = fmaxf(mt, wave_xor32(mt));
-            const float m_new = fmaxf(m, mt);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float mc = m_use * c;
-            // ---- rescale what was accumulated under the old max (skipped when no max moved: alpha == 1)
-            const float alpha = __builtin_amdgcn_exp2f(m * c - mc);
-            if (__any(m_new > m)) {
-#pragma unroll
-                for (int db = 0; db < T::NDB; ++db) acc[db] *= alpha;
-                l *= alpha;
-            }
+            const bool moved = __any(mt * c > m * c + RESCALE_SLACK);   // also true for a first visible key
+            const float m_new = moved ? fmaxf(m, mt) : m;
+            const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * c);   // 1 if unmoved
             m = m_new;
-            // ---- probabilities (fp32 sum for l, bf16 for the P.V product)
-            u32x4 pf[T::NKB][2];
+            const float mc = m == -INFINITY ? 0.f : m * c;
             float rs = 0.f;
 #pragma unroll
             for (int kb = 0; kb < T::NKB; ++kb) {
@@ -284,29 +286,77 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void fwd_bf16_kernel(FwdArgs a
                 for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                     for (int w = 0; w < 4; ++w)
-                        pf[kb][ks][w] = pack_bf16(s[kb][8 * ks + 2 * w], s[kb][8 * ks + 2 * w + 1]);
+                        p_next[kb][ks][w] = pack_bf16(s[kb][8 * ks + 2 * w], s[kb][8 * ks + 2 * w + 1]);
             }
-            l += rs;
-            // ---- O^T += V^T P^T
-            const char* vt = buf + T::KBYTES;
+            l = __builtin_fmaf(l, alpha, rs);
+            alpha_prev = alpha;
+            moved_prev = moved;
+        }
+        if constexpr (DO_PV) {   // O^T += V^T P^T for tile t-1; V^T operand by two transpose reads
 #pragma unroll
             for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                     for (int db = 0; db < T::NDB; ++db) {
-                        const bf16x8 vf = as_bf16x8(lds_read16(vt, v_off<D>(32 * db + col, 4 * kb + 2 * ks + h)));
-                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pf[kb][ks]), acc[db], 0, 0, 0);
+                        const char* p = vbuf + v_roff[db] + (32 * kb + 16 * ks) * T::ROW;
+                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * T::ROW));
+                        const u32x4 vv = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                                          __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), as_bf16x8(p_cur[kb][ks]),
+                                                                          acc[db], 0, 0, 0);
                     }
         }
-        if (t + 1 < ntiles) {
-            store_tile<D>(st, smem + ((t + 1) & 1) * T::BUF, tid);
-            if (t + 2 < ntiles) load_tile<D>(st, kh, vh, (t + 2) * T::BC, a.n_kv, tid);
+        if constexpr (DO_S) {
+            // keep the new weights inside this block (an empty statement that reads them), so that they are
+            // not sunk past the P.V MFMAs above; then they become the next step's P.V operand
+#pragma unroll
+            for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    __asm__ volatile("" ::"v"(p_next[kb][ks][0]), "v"(p_next[kb][ks][1]), "v"(p_next[kb][ks][2]),
+                                     "v"(p_next[kb][ks][3]));
+                    p_cur[kb][ks] = p_next[kb][ks];
+                }
         }
+    };
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+
+    if (ntiles > 0) issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
+    if (ntiles > 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * T::SEGS_PER_WAVE));   // vmcnt(tile-1 loads)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                                         // vmcnt(0)
+    __syncthreads();
+
+    // Every wave's loads of tile t+1 have landed and every wave is done with K_t and V_{t-1} after the
+    // barrier at the end of iteration t, so tile t+2 may then be loaded into their buffers.  All waves run
+    // exactly ntiles such barriers, whether or not they still have tiles to compute.
+    auto retire = [&](int t) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         __syncthreads();
+        if (t + 2 < ntiles) issue_tile(t + 2);
+    };
+    auto kbuf_of = [&](int t) { return (const char*)(smem + (t & 1) * T::TILE); };
+    auto vbuf_of = [&](int t) { return (const char*)(smem + 2 * T::TILE + (t % 3) * T::TILE); };
+    // the steady-state iteration: buffers passed as restrict-qualified pointers, distinct from those the
+    // loads issued by retire() write (tile t+2), so the compiler does not wait for those loads before
+    // reading tile t / t-1 (the explicit vmcnt(0) before every barrier is what makes that true)
+    auto iterate = [&](int t, const char* __restrict__ kb, const char* __restrict__ vb) {
+        step(yes{}, yes{}, t * T::BC + T::BC > wave_full_end, t, kb, vb);
+        retire(t);
+    };
+    int t = 0;
+    if (ntiles > 0) {
+        if (wave_tiles > 0) step(yes{}, no{}, T::BC > wave_full_end, 0, kbuf_of(0), vbuf_of(2));
+        retire(0);
+        for (t = 1; t < wave_tiles; ++t) iterate(t, kbuf_of(t), vbuf_of(t - 1));
+        if (wave_tiles > 0) step(no{}, yes{}, false, t, kbuf_of(t), vbuf_of(t - 1));   // P.V of the last tile
+        for (t = max(t, 1); t < ntiles; ++t) retire(t);
     }
 
-    // ---- epilogue: one division by the final denominator; lse = scaled max + ln(l)
+    // ---- epilogue: one division by the final denominator; lse = scaled reference + ln(l)
     const float l_tot = l + wave_xor32(l);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (q_ok) {
@@ -341,11 +391,12 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
     const int num_qt = (a.n_q + T::BR - 1) / T::BR;
     const long long total_ll = (long long)num_qt * a.bh;
     if (total_ll > 0x7fffffffLL - NXCD) return hipErrorInvalidValue;
+    if ((long long)a.n_kv * T::ROW > 0x7fffffffLL) return hipErrorInvalidValue;   // buffer bound is 31-bit
     const int total = (int)total_ll;
     const int per_xcd = (total + NXCD - 1) / NXCD;
     const int grid = per_xcd * NXCD;
     auto kern = fwd_bf16_kernel<D, CAUSAL, OUT_F32>;
-    static bool attr_set = false;   // LDS above 64 KiB needs an explicit opt-in
+    static bool attr_set = false;   // LDS above the default limit needs an explicit opt-in
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
