@@ -23,9 +23,12 @@ SOURCES = ["attn_api.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_merge.
 
 # Packed fp32 VALU instructions are switched off for all device code (the compiler would otherwise form
 # them from ordinary float code); the host pass warns that it does not know the feature, which is harmless.
+# MFMA results are allocated to ordinary VGPRs where possible (the softmax reads the score accumulators
+# with VALU instructions; accumulators parked in AGPRs would need a copy per element and tile).
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

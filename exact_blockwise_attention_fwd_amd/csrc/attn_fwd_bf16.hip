@@ -7,7 +7,10 @@
 // Attention", section 3, Transform stage) is bottom-right aligned; tiles wholly in the future are skipped.
 //
 // Mapping to CDNA4 (gfx950), designed for this chip rather than taken from the pages' GPU:
-//  * A workgroup is 4 wave64s and owns 128 query rows of one (b, h); each wave owns 32 rows.
+//  * A workgroup is 4 wave64s.  Each wave owns QB blocks of 32 query rows of one (b, h): QB = 2 for d = 128
+//    (one wave per SIMD, ~360 registers with the output accumulators in AGPRs), QB = 1 for d = 64.  Every
+//    K or V operand read from LDS feeds QB MFMAs, which is what keeps LDS bandwidth (the transpose read
+//    below runs at half the rate of a plain 16-byte read) off the critical path at d = 128.
 //  * Everything is computed transposed.  S^T = K Q^T uses v_mfma_f32_32x32x16_bf16 with A = K rows from
 //    LDS and B = Q^T held in registers for the whole key loop.  In the 32x32 accumulator layout a lane then
 //    holds 16 keys of ONE query (lane l and l^32 share query l%32), so the row max and row sum are in-lane
@@ -25,8 +28,11 @@
 //    store instructions, and loads past the last key return zeros (the buffer resource's bound).  Each
 //    wave instruction fills one contiguous 1 KiB LDS segment in lane order, so the XOR swizzle of the LDS
 //    layout is applied by choosing which 16-byte global chunk each lane fetches.
-//  * Tiles are double-buffered: the loads of tile t+2 are issued right after the barrier that retires tile
-//    t, and land while tile t+1 is computed; one workgroup barrier per tile.
+//  * K is double-buffered and V triple-buffered.  Iteration t computes S(t) and the weights of tile t, and
+//    the P.V product of tile t-1 (software pipelining: the softmax of one tile shares a basic block with
+//    the P.V MFMAs of the previous one, so the VALU and the matrix cores overlap inside one wave).  After
+//    the barrier that ends iteration t, tile t+2 is loaded into the buffers of K_t and V_{t-1}; it has a
+//    whole iteration to land.
 //  * LDS rows are XOR-swizzled in 16-byte units so that the operand reads of each 16-lane block (K rows for
 //    S^T, four V rows for the transpose read) hit distinct banks.
 //  * exp is v_exp_f32 (base 2) with scale*log2(e) folded into one FMA per score.  The running max used as
@@ -57,7 +63,9 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_SLACK = 8.0f;   // exp2 units the exponent reference may lag the running max
@@ -66,10 +74,12 @@ constexpr unsigned BUF_RSRC_WORD3 = 0x00020000u;   // raw buffer, 32-bit data fo
 
 template <int D>
 struct Tile {
+    static constexpr int QB = D == 128 ? 2 : 1;      // 32-row query blocks per wave
     static constexpr int NW = 4;                     // waves per workgroup
     static constexpr int THREADS = 64 * NW;
-    static constexpr int BR = 32 * NW;               // query rows per workgroup
-    static constexpr int BC = D == 128 ? 64 : 128;   // keys per tile
+    static constexpr int WAVES_PER_SIMD = QB == 2 ? 1 : 2;
+    static constexpr int BR = 32 * QB * NW;          // query rows per workgroup
+    static constexpr int BC = D == 128 ? 32 : 128;   // keys per tile
     static constexpr int NKB = BC / 32;              // 32-key blocks of S^T per tile
     static constexpr int NDB = D / 32;               // 32-row blocks of O^T
     static constexpr int NKS = D / 16;               // k-steps of S^T (over d)
@@ -81,7 +91,7 @@ struct Tile {
     static constexpr int LPR = ROW / 16;             // lanes (16-byte chunks) per row
     static constexpr int LDS = 5 * TILE;             // K double-buffered, then V triple-buffered
     static_assert(SEGS % NW == 0, "segments split evenly over the waves");
-    static_assert(TILE == 16384, "both configurations use 16 KiB tiles");
+    static_assert(NW * RPS * ROW == 4096, "a wave's load segments are 4 KiB apart");
 };
 
 // bits 2 and 3 of a row index swapped (an involution)
@@ -112,10 +122,12 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
 template <int D, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(Tile<D>::THREADS, 2) void fwd_bf16_kernel(FwdArgs a, int num_qt, int total,
-                                                                      int per_xcd) {
+__global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd_bf16_kernel(FwdArgs a, int num_qt,
+                                                                                            int total, int per_xcd) {
     using T = Tile<D>;
+    constexpr int QB = T::QB;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
+    lds_char* const lds = (lds_char*)smem;   // all LDS addressing stays in the LDS address space
 
     // XCD-aware remap: hardware workgroup w runs on XCD w % 8; give each XCD a contiguous logical range
     const int w_hw = blockIdx.x;
@@ -129,12 +141,10 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void fwd_bf16_kernel(FwdArgs a
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;                         // half-wave
-    const int col = lane & 31;                       // query slot within the wave
+    const int col = lane & 31;                       // query slot within a 32-row block
 
     const int q0 = qt * T::BR;
-    const int qw0 = q0 + 32 * wave;                  // first query of this wave
-    const int qi = qw0 + col;                        // this lane's query
-    const bool q_ok = qi < a.n_q;
+    const int qw0 = q0 + 32 * QB * wave;             // first query of this wave; block qb starts at qw0+32qb
 
     const uint16_t* qh = static_cast<const uint16_t*>(a.q) + (size_t)bh * a.q_head_stride;
     const uint16_t* kh = static_cast<const uint16_t*>(a.k) + (size_t)bh * a.kv_head_stride;
@@ -147,9 +157,9 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void fwd_bf16_kernel(FwdArgs a
     const int ntiles = (kv_end + T::BC - 1) / T::BC;
 
     // per-wave visibility bounds (wave-uniform)
-    const int qw_last = min(qw0 + 31, a.n_q - 1);
-    const int wave_key_end = qw0 >= a.n_q ? 0 : CAUSAL ? min(kv_end, qw_last + a.offset + 1) : kv_end;   // exclusive
-    const int wave_full_end = CAUSAL ? min(a.n_kv, qw0 + a.offset + 1) : a.n_kv;      // keys < this: all visible
+    const int qw_last = min(qw0 + 32 * QB - 1, a.n_q - 1);
+    const int wave_key_end = qw0 >= a.n_q ? 0 : CAUSAL ? min(kv_end, qw_last + a.offset + 1) : kv_end;
+    const int wave_full_end = CAUSAL ? min(a.n_kv, qw0 + a.offset + 1) : a.n_kv;   // keys < this: all visible
 
     // ---- global -> LDS loads.  Each tile gets buffer resources whose base is the tile's first key and whose
     // bound is the rest of this head's key range, so loads past the last key return zeros; the whole
@@ -166,8 +176,8 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void fwd_bf16_kernel(FwdArgs a
         v_voff = r0 * T::ROW + 16 * (p ^ v_swz<D>(r0));
     }
     auto issue_tile = [&](int t) {
-        char* kbuf = smem + (t & 1) * T::TILE;
-        char* vbuf = smem + 2 * T::TILE + (t % 3) * T::TILE;
+        lds_char* kbuf = lds + (t & 1) * T::TILE;
+        lds_char* vbuf = lds + 2 * T::TILE + (t % 3) * T::TILE;
         const long long base = (long long)t * T::TILE;
         const int left = (int)(kv_bytes - base);
         const __amdgpu_buffer_rsrc_t krs =
@@ -182,18 +192,23 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void fwd_bf16_kernel(FwdArgs a
         }
     };
 
-    // ---- Q^T fragments (B operand): query qi, head-dim elements 16*ks + 8*h .. +7.
+    // ---- Q^T fragments (B operand): query qw0+32qb+col, head-dim elements 16*ks + 8*h .. +7.
     // A negative scale negates Q (exact in bf16) so that every exponent is taken against a running max;
     // a zero scale zeroes Q, which gives the same all-zero logits without multiplying -inf by zero.
     const float scale_abs = fabsf(a.scale);
     const unsigned neg = a.scale < 0.f ? 0x80008000u : 0u;
     const unsigned keep = a.scale == 0.f ? 0u : 0xffffffffu;
-    bf16x8 qf[T::NKS];
+    bf16x8 qf[QB][T::NKS];
 #pragma unroll
-    for (int ks = 0; ks < T::NKS; ++ks) {
-        u32x4 x = q_ok ? *reinterpret_cast<const u32x4*>(qh + (size_t)qi * D + 16 * ks + 8 * h) : u32x4{0, 0, 0, 0};
-        x = (x ^ neg) & keep;
-        qf[ks] = as_bf16x8(x);
+    for (int qb = 0; qb < QB; ++qb) {
+        const int qi = qw0 + 32 * qb + col;
+#pragma unroll
+        for (int ks = 0; ks < T::NKS; ++ks) {
+            u32x4 x = qi < a.n_q ? *reinterpret_cast<const u32x4*>(qh + (size_t)qi * D + 16 * ks + 8 * h)
+                                 : u32x4{0, 0, 0, 0};
+            x = (x ^ neg) & keep;
+            qf[qb][ks] = as_bf16x8(x);
+        }
     }
     const float c = a.scale == 0.f ? LOG2E : scale_abs * LOG2E;   // scale * log2(e), always > 0
 
@@ -214,12 +229,18 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void fwd_bf16_kernel(FwdArgs a
         }
     }
 
-    f32x16 acc[T::NDB];
+    f32x16 acc[QB][T::NDB];
 #pragma unroll
-    for (int db = 0; db < T::NDB; ++db) acc[db] = f32x16{};
-    float m = -INFINITY;   // exponent reference: running max of this query's raw dot products (may lag)
-    float l = 0.f;         // running denominator against m, this half-wave's keys only
-    u32x4 p_cur[T::NKB][2];   // bf16 weights of the previous tile, consumed by its P.V one iteration later
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int db = 0; db < T::NDB; ++db) acc[qb][db] = f32x16{};
+    float m[QB], l[QB];   // exponent reference (running max of raw dot products, may lag) and denominator
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        m[qb] = -INFINITY;
+        l[qb] = 0.f;      // this half-wave's keys only; the halves are added at the end
+    }
+    u32x4 p_cur[QB][T::NKB][2];   // bf16 weights of the previous tile, consumed by its P.V one step later
 
     // Tiles this wave computes: a prefix [0, wave_tiles) of the workgroup's ntiles (causal waves stop early).
     const int wave_tiles = min(ntiles, (wave_key_end + T::BC - 1) / T::BC);
@@ -229,67 +250,106 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void fwd_bf16_kernel(FwdArgs a
     // MFMAs of tile t-1 are independent and sit in one straight-line block, so the compiler can issue the
     // softmax instructions while the matrix cores run.  An output rescale caused by tile t is applied at
     // the start of the next step, i.e. after P.V(t-1) (old reference) and before P.V(t) (new reference).
-    float alpha_prev = 1.f;
+    float alpha_prev[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) alpha_prev[qb] = 1.f;
     bool moved_prev = false;
-    auto step = [&](auto do_s, auto do_pv, bool masked, int t, const char* __restrict__ kbuf,
-                    const char* __restrict__ vbuf) {
+    auto step = [&](auto do_s, auto do_pv, bool masked, int t, const lds_char* __restrict__ kbuf,
+                    const lds_char* __restrict__ vbuf) {
         constexpr bool DO_S = decltype(do_s)::value, DO_PV = decltype(do_pv)::value;
+        // Per-lane LDS offsets pass through an empty statement here, so that the compiler forms
+        // "buffer + offset" once per step and folds the (kb, ks) constants into the instructions' offset
+        // fields, instead of hoisting every offset+constant combination out of the loop.
+        int kro[T::NKS], vro[T::NDB];
+#pragma unroll
+        for (int ks = 0; ks < T::NKS; ++ks) {
+            kro[ks] = k_roff[ks];
+            __asm__ volatile("" : "+v"(kro[ks]));
+        }
+#pragma unroll
+        for (int db = 0; db < T::NDB; ++db) {
+            vro[db] = v_roff[db];
+            __asm__ volatile("" : "+v"(vro[db]));
+        }
         if (moved_prev) {
 #pragma unroll
-            for (int db = 0; db < T::NDB; ++db) acc[db] *= alpha_prev;
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int db = 0; db < T::NDB; ++db) acc[qb][db] *= alpha_prev[qb];
         }
-        f32x16 s[T::NKB];
-        u32x4 p_next[T::NKB][2];
+        f32x16 s[QB][T::NKB];
+        u32x4 p_next[QB][T::NKB][2];
         if constexpr (DO_S) {
             const int kt = t * T::BC;
 #pragma unroll
-            for (int kb = 0; kb < T::NKB; ++kb) s[kb] = f32x16{};
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int kb = 0; kb < T::NKB; ++kb) s[qb][kb] = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < T::NKS; ++ks) {
 #pragma unroll
                 for (int kb = 0; kb < T::NKB; ++kb) {
-                    const u32x4 kv = *reinterpret_cast<const u32x4*>(kbuf + k_roff[ks] + 32 * kb * T::ROW);
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qf[ks], s[kb], 0, 0, 0);
+                    const u32x4 kv = *(const lds_u32x4*)(kbuf + kro[ks] + 32 * kb * T::ROW);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
+                        s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qf[qb][ks], s[qb][kb], 0, 0, 0);
                 }
             }
             if (masked) {   // keys past the end or in the causal future
-                const int lim = CAUSAL ? min(a.n_kv - 1, qi + a.offset) : a.n_kv - 1;   // last visible key
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    const int qi = qw0 + 32 * qb + col;
+                    const int lim = CAUSAL ? min(a.n_kv - 1, qi + a.offset) : a.n_kv - 1;   // last visible key
+#pragma unroll
+                    for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) {
+                            const int key = kt + 32 * kb + 16 * (j >> 3) + 8 * h + (j & 7);
+                            if (key > lim) s[qb][kb][j] = -INFINITY;
+                        }
+                }
+            }
+            // tile max; the reference moves (for every row of the wave) only when some row outgrew it
+            float mt[QB];
+            bool grow = false;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                mt[qb] = -INFINITY;
 #pragma unroll
                 for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const int key = kt + 32 * kb + 16 * (j >> 3) + 8 * h + (j & 7);
-                        if (key > lim) s[kb][j] = -INFINITY;
-                    }
+                    for (int j = 0; j < 16; ++j) mt[qb] = fmaxf(mt[qb], s[qb][kb][j]);
+                mt[qb] = fmaxf(mt[qb], wave_xor32(mt[qb]));
+                grow = grow || (mt[qb] * c > m[qb] * c + RESCALE_SLACK);   // also true for a first visible key
             }
-            // tile max; the reference moves (for every row of the wave) only when some row outgrew it
-            float mt = -INFINITY;
+            const bool moved = __any(grow);
 #pragma unroll
-            for (int kb = 0; kb < T::NKB; ++kb)
+            for (int qb = 0; qb < QB; ++qb) {
+                const float m_new = moved ? fmaxf(m[qb], mt[qb]) : m[qb];
+                const float alpha = m[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m[qb] - m_new) * c);
+                m[qb] = m_new;
+                const float mc = m_new == -INFINITY ? 0.f : m_new * c;
+                float rs = 0.f;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) mt = fmaxf(mt, s[kb][j]);
-            mt = fmaxf(mt, wave_xor32(mt));
-            const bool moved = __any(mt * c > m * c + RESCALE_SLACK);   // also true for a first visible key
-            const float m_new = moved ? fmaxf(m, mt) : m;
-            const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * c);   // 1 if unmoved
-            m = m_new;
-            const float mc = m == -INFINITY ? 0.f : m * c;
-            float rs = 0.f;
+                for (int kb = 0; kb < T::NKB; ++kb) {
 #pragma unroll
-            for (int kb = 0; kb < T::NKB; ++kb) {
+                    for (int j = 0; j < 16; ++j) s[qb][kb][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][j], c, -mc));
+                    // pairwise sum (short dependency chains)
+                    float r8[8];
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    s[kb][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][j], c, -mc));
-                    rs += s[kb][j];
+                    for (int j = 0; j < 8; ++j) r8[j] = s[qb][kb][2 * j] + s[qb][kb][2 * j + 1];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) r8[j] = r8[2 * j] + r8[2 * j + 1];
+                    rs += (r8[0] + r8[1]) + (r8[2] + r8[3]);
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                        for (int w = 0; w < 4; ++w)
+                            p_next[qb][kb][ks][w] = pack_bf16(s[qb][kb][8 * ks + 2 * w], s[qb][kb][8 * ks + 2 * w + 1]);
                 }
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                    for (int w = 0; w < 4; ++w)
-                        p_next[kb][ks][w] = pack_bf16(s[kb][8 * ks + 2 * w], s[kb][8 * ks + 2 * w + 1]);
+                l[qb] = __builtin_fmaf(l[qb], alpha, rs);
+                alpha_prev[qb] = alpha;
             }
-            l = __builtin_fmaf(l, alpha, rs);
-            alpha_prev = alpha;
             moved_prev = moved;
         }
         if constexpr (DO_PV) {   // O^T += V^T P^T for tile t-1; V^T operand by two transpose reads
@@ -299,26 +359,32 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void fwd_bf16_kernel(FwdArgs a
                 for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                     for (int db = 0; db < T::NDB; ++db) {
-                        const char* p = vbuf + v_roff[db] + (32 * kb + 16 * ks) * T::ROW;
+                        const lds_char* p = vbuf + vro[db] + (32 * kb + 16 * ks) * T::ROW;
                         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
                         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * T::ROW));
                         const u32x4 vv = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
                                           __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
-                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), as_bf16x8(p_cur[kb][ks]),
-                                                                          acc[db], 0, 0, 0);
+#pragma unroll
+                        for (int qb = 0; qb < QB; ++qb)
+                            acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), as_bf16x8(p_cur[qb][kb][ks]),
+                                                                              acc[qb][db], 0, 0, 0);
                     }
         }
         if constexpr (DO_S) {
             // keep the new weights inside this block (an empty statement that reads them), so that they are
             // not sunk past the P.V MFMAs above; then they become the next step's P.V operand
 #pragma unroll
-            for (int kb = 0; kb < T::NKB; ++kb)
+            for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    __asm__ volatile("" ::"v"(p_next[kb][ks][0]), "v"(p_next[kb][ks][1]), "v"(p_next[kb][ks][2]),
-                                     "v"(p_next[kb][ks][3]));
-                    p_cur[kb][ks] = p_next[kb][ks];
-                }
+                for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        __asm__ volatile("" ::"v"(p_next[qb][kb][ks][0]), "v"(p_next[qb][kb][ks][1]),
+                                         "v"(p_next[qb][kb][ks][2]), "v"(p_next[qb][kb][ks][3]));
+                        p_cur[qb][kb][ks] = p_next[qb][kb][ks];
+                    }
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) __asm__ volatile("" ::"v"(l[qb]));
         }
     };
     using yes = std::integral_constant<bool, true>;
@@ -338,12 +404,12 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void fwd_bf16_kernel(FwdArgs a
         __syncthreads();
         if (t + 2 < ntiles) issue_tile(t + 2);
     };
-    auto kbuf_of = [&](int t) { return (const char*)(smem + (t & 1) * T::TILE); };
-    auto vbuf_of = [&](int t) { return (const char*)(smem + 2 * T::TILE + (t % 3) * T::TILE); };
-    // the steady-state iteration: buffers passed as restrict-qualified pointers, distinct from those the
+    auto kbuf_of = [&](int t) { return (const lds_char*)(lds + (t & 1) * T::TILE); };
+    auto vbuf_of = [&](int t) { return (const lds_char*)(lds + 2 * T::TILE + (t % 3) * T::TILE); };
+    // The steady-state iteration gets its buffers as restrict-qualified pointers, distinct from those the
     // loads issued by retire() write (tile t+2), so the compiler does not wait for those loads before
-    // reading tile t / t-1 (the explicit vmcnt(0) before every barrier is what makes that true)
-    auto iterate = [&](int t, const char* __restrict__ kb, const char* __restrict__ vb) {
+    // reading tile t and t-1 (the explicit vmcnt(0) before every barrier is what makes that true).
+    auto iterate = [&](int t, const lds_char* __restrict__ kb, const lds_char* __restrict__ vb) {
         step(yes{}, yes{}, t * T::BC + T::BC > wave_full_end, t, kb, vb);
         retire(t);
     };
@@ -357,31 +423,37 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 2) void fwd_bf16_kernel(FwdArgs a
     }
 
     // ---- epilogue: one division by the final denominator; lse = scaled reference + ln(l)
-    const float l_tot = l + wave_xor32(l);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (q_ok) {
-        if (OUT_F32) {
-            float* oh = static_cast<float*>(a.o) + (size_t)bh * a.q_head_stride + (size_t)qi * D;
 #pragma unroll
-            for (int db = 0; db < T::NDB; ++db)
+    for (int qb = 0; qb < QB; ++qb) {
+        const int qi = qw0 + 32 * qb + col;
+        const float l_tot = l[qb] + wave_xor32(l[qb]);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        if (qi < a.n_q) {
+            if (OUT_F32) {
+                float* oh = static_cast<float*>(a.o) + (size_t)bh * a.q_head_stride + (size_t)qi * D;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    f32x4 o4 = {acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv, acc[db][4 * g + 2] * inv,
-                                acc[db][4 * g + 3] * inv};
-                    *reinterpret_cast<f32x4*>(oh + 32 * db + 8 * g + 4 * h) = o4;
-                }
-        } else {
-            uint16_t* oh = static_cast<uint16_t*>(a.o) + (size_t)bh * a.q_head_stride + (size_t)qi * D;
+                for (int db = 0; db < T::NDB; ++db)
 #pragma unroll
-            for (int db = 0; db < T::NDB; ++db)
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x16& ac = acc[qb][db];
+                        f32x4 o4 = {ac[4 * g] * inv, ac[4 * g + 1] * inv, ac[4 * g + 2] * inv, ac[4 * g + 3] * inv};
+                        *reinterpret_cast<f32x4*>(oh + 32 * db + 8 * g + 4 * h) = o4;
+                    }
+            } else {
+                uint16_t* oh = static_cast<uint16_t*>(a.o) + (size_t)bh * a.q_head_stride + (size_t)qi * D;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    u32x2 o2 = {pack_bf16(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv),
-                                pack_bf16(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
-                    *reinterpret_cast<u32x2*>(oh + 32 * db + 8 * g + 4 * h) = o2;
-                }
+                for (int db = 0; db < T::NDB; ++db)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x16& ac = acc[qb][db];
+                        u32x2 o2 = {pack_bf16(ac[4 * g] * inv, ac[4 * g + 1] * inv),
+                                    pack_bf16(ac[4 * g + 2] * inv, ac[4 * g + 3] * inv)};
+                        *reinterpret_cast<u32x2*>(oh + 32 * db + 8 * g + 4 * h) = o2;
+                    }
+            }
+            if (h == 0)
+                a.lse[(size_t)bh * a.n_q + qi] = l_tot > 0.f ? m[qb] * scale_abs + logf(l_tot) : -INFINITY;
         }
-        if (h == 0) a.lse[(size_t)bh * a.n_q + qi] = l_tot > 0.f ? m * scale_abs + logf(l_tot) : -INFINITY;
     }
 }
 
