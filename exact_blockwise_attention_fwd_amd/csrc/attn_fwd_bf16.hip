@@ -68,18 +68,18 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr float RESCALE_SLACK = 8.0f;   // exp2 units the exponent reference may lag the running max
+constexpr float REF_BOUND = 18446744073709551616.0f;   // 2^64: largest weight sum taken against a stale reference
 constexpr int NXCD = 8;
 constexpr unsigned BUF_RSRC_WORD3 = 0x00020000u;   // raw buffer, 32-bit data format, bounds-checked
 
 template <int D>
 struct Tile {
-    static constexpr int QB = D == 128 ? 2 : 1;      // 32-row query blocks per wave
+    static constexpr int QB = 1;      // 32-row query blocks per wave
     static constexpr int NW = 4;                     // waves per workgroup
     static constexpr int THREADS = 64 * NW;
     static constexpr int WAVES_PER_SIMD = QB == 2 ? 1 : 2;
     static constexpr int BR = 32 * QB * NW;          // query rows per workgroup
-    static constexpr int BC = D == 128 ? 32 : 128;   // keys per tile
+    static constexpr int BC = D == 128 ? 64 : 128;   // keys per tile
     static constexpr int NKB = BC / 32;              // 32-key blocks of S^T per tile
     static constexpr int NDB = D / 32;               // 32-row blocks of O^T
     static constexpr int NKS = D / 16;               // k-steps of S^T (over d)
@@ -245,18 +245,25 @@ __global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd
     // Tiles this wave computes: a prefix [0, wave_tiles) of the workgroup's ntiles (causal waves stop early).
     const int wave_tiles = min(ntiles, (wave_key_end + T::BC - 1) / T::BC);
 
-    // One pipelined step at tile t: S(t) = K_t Q^T, the new exponent reference, the weights of tile t, and
-    // the P.V product of tile t-1 (weights from the previous step).  The weights of tile t and the P.V
-    // MFMAs of tile t-1 are independent and sit in one straight-line block, so the compiler can issue the
-    // softmax instructions while the matrix cores run.  An output rescale caused by tile t is applied at
-    // the start of the next step, i.e. after P.V(t-1) (old reference) and before P.V(t) (new reference).
+    // One pipelined step at tile t: S(t) = K_t Q^T, the P.V product of tile t-1 (weights from the previous
+    // step), then the weights of tile t.  In program order the MFMAs of both products come first and the
+    // softmax last, all in one straight-line block: the softmax waits only for S(t) and then issues while
+    // the P.V MFMAs run.  An output rescale caused by tile t is applied at the start of the next step, i.e.
+    // after P.V(t-1) (old reference) and before P.V(t) (new reference).
+    //
+    // The exponent reference m is not recomputed from every tile: the weights exp2(s*c - m*c) are taken
+    // against the current reference, and only if no reference exists yet or some weight sum exceeds 2^64
+    // (a score more than 64 exp2-units above the reference) is the tile redone against its true max.  Every
+    // weight is then below 2^64 and the accumulated sums stay far inside fp32 range, so the result equals
+    // the running-max formulation up to rounding; the row max drops out of the common path.
     float alpha_prev[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) alpha_prev[qb] = 1.f;
     bool moved_prev = false;
-    auto step = [&](auto do_s, auto do_pv, bool masked, int t, const lds_char* __restrict__ kbuf,
+    auto step = [&](auto do_s, auto do_pv, auto masked_c, int t, const lds_char* __restrict__ kbuf,
                     const lds_char* __restrict__ vbuf) {
         constexpr bool DO_S = decltype(do_s)::value, DO_PV = decltype(do_pv)::value;
+        constexpr bool MASKED = decltype(masked_c)::value;
         // Per-lane LDS offsets pass through an empty statement here, so that the compiler forms
         // "buffer + offset" once per step and folds the (kb, ks) constants into the instructions' offset
         // fields, instead of hoisting every offset+constant combination out of the loop.
@@ -276,11 +283,10 @@ __global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd
             for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
                 for (int db = 0; db < T::NDB; ++db) acc[qb][db] *= alpha_prev[qb];
+            moved_prev = false;
         }
         f32x16 s[QB][T::NKB];
-        u32x4 p_next[QB][T::NKB][2];
         if constexpr (DO_S) {
-            const int kt = t * T::BC;
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -295,62 +301,6 @@ __global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd
                         s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qf[qb][ks], s[qb][kb], 0, 0, 0);
                 }
             }
-            if (masked) {   // keys past the end or in the causal future
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    const int qi = qw0 + 32 * qb + col;
-                    const int lim = CAUSAL ? min(a.n_kv - 1, qi + a.offset) : a.n_kv - 1;   // last visible key
-#pragma unroll
-                    for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-                        for (int j = 0; j < 16; ++j) {
-                            const int key = kt + 32 * kb + 16 * (j >> 3) + 8 * h + (j & 7);
-                            if (key > lim) s[qb][kb][j] = -INFINITY;
-                        }
-                }
-            }
-            // tile max; the reference moves (for every row of the wave) only when some row outgrew it
-            float mt[QB];
-            bool grow = false;
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                mt[qb] = -INFINITY;
-#pragma unroll
-                for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) mt[qb] = fmaxf(mt[qb], s[qb][kb][j]);
-                mt[qb] = fmaxf(mt[qb], wave_xor32(mt[qb]));
-                grow = grow || (mt[qb] * c > m[qb] * c + RESCALE_SLACK);   // also true for a first visible key
-            }
-            const bool moved = __any(grow);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const float m_new = moved ? fmaxf(m[qb], mt[qb]) : m[qb];
-                const float alpha = m[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m[qb] - m_new) * c);
-                m[qb] = m_new;
-                const float mc = m_new == -INFINITY ? 0.f : m_new * c;
-                float rs = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < T::NKB; ++kb) {
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) s[qb][kb][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][j], c, -mc));
-                    // pairwise sum (short dependency chains)
-                    float r8[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) r8[j] = s[qb][kb][2 * j] + s[qb][kb][2 * j + 1];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) r8[j] = r8[2 * j] + r8[2 * j + 1];
-                    rs += (r8[0] + r8[1]) + (r8[2] + r8[3]);
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                        for (int w = 0; w < 4; ++w)
-                            p_next[qb][kb][ks][w] = pack_bf16(s[qb][kb][8 * ks + 2 * w], s[qb][kb][8 * ks + 2 * w + 1]);
-                }
-                l[qb] = __builtin_fmaf(l[qb], alpha, rs);
-                alpha_prev[qb] = alpha;
-            }
-            moved_prev = moved;
         }
         if constexpr (DO_PV) {   // O^T += V^T P^T for tile t-1; V^T operand by two transpose reads
 #pragma unroll
@@ -371,20 +321,88 @@ __global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd
                     }
         }
         if constexpr (DO_S) {
-            // keep the new weights inside this block (an empty statement that reads them), so that they are
-            // not sunk past the P.V MFMAs above; then they become the next step's P.V operand
+            if constexpr (MASKED) {   // keys past the end or in the causal future
+                const int kt = t * T::BC;
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    const int qi = qw0 + 32 * qb + col;
+                    const int lim = CAUSAL ? min(a.n_kv - 1, qi + a.offset) : a.n_kv - 1;   // last visible key
+#pragma unroll
+                    for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) {
+                            const int key = kt + 32 * kb + 16 * (j >> 3) + 8 * h + (j & 7);
+                            if (key > lim) s[qb][kb][j] = -INFINITY;
+                        }
+                }
+            }
+            u32x4 p_next[QB][T::NKB][2];
+            float rs[QB];
+            // weights of tile t against reference m (m*c == mc; 0 stands in while no reference exists)
+            auto weights = [&](const float (&mc)[QB]) {
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    rs[qb] = 0.f;
+#pragma unroll
+                    for (int kb = 0; kb < T::NKB; ++kb) {
+                        float e[16];
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][j], c, -mc[qb]));
+                        float r8[8];   // pairwise row sum (short dependency chains)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) r8[j] = e[2 * j] + e[2 * j + 1];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) r8[j] = r8[2 * j] + r8[2 * j + 1];
+                        rs[qb] += (r8[0] + r8[1]) + (r8[2] + r8[3]);
+#pragma unroll
+                        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                            for (int w = 0; w < 4; ++w)
+                                p_next[qb][kb][ks][w] = pack_bf16(e[8 * ks + 2 * w], e[8 * ks + 2 * w + 1]);
+                    }
+                }
+            };
+            float mc[QB];
+            bool redo = false;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                mc[qb] = m[qb] == -INFINITY ? 0.f : m[qb] * c;
+                redo = redo || m[qb] == -INFINITY;
+            }
+            weights(mc);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) redo = redo || !(rs[qb] <= REF_BOUND);
+            float alpha[QB];
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) alpha[qb] = 1.f;
+            if (__any(redo)) {
+                // rare: the first visible keys, or a score far above the reference.  Move the reference to
+                // the running max (for every row of the wave) and recompute the weights.
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    float mt = -INFINITY;
+#pragma unroll
+                    for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) mt = fmaxf(mt, s[qb][kb][j]);
+                    mt = fmaxf(mt, wave_xor32(mt));
+                    const float m_new = fmaxf(m[qb], mt);
+                    alpha[qb] = m[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m[qb] - m_new) * c);
+                    m[qb] = m_new;
+                    mc[qb] = m_new == -INFINITY ? 0.f : m_new * c;
+                    alpha_prev[qb] = alpha[qb];
+                }
+                moved_prev = true;
+                weights(mc);
+            }
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) l[qb] = __builtin_fmaf(l[qb], alpha[qb], rs[qb]);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
                 for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        __asm__ volatile("" ::"v"(p_next[qb][kb][ks][0]), "v"(p_next[qb][kb][ks][1]),
-                                         "v"(p_next[qb][kb][ks][2]), "v"(p_next[qb][kb][ks][3]));
-                        p_cur[qb][kb][ks] = p_next[qb][kb][ks];
-                    }
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) __asm__ volatile("" ::"v"(l[qb]));
+                    for (int ks = 0; ks < 2; ++ks) p_cur[qb][kb][ks] = p_next[qb][kb][ks];
         }
     };
     using yes = std::integral_constant<bool, true>;
@@ -410,15 +428,25 @@ __global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd
     // loads issued by retire() write (tile t+2), so the compiler does not wait for those loads before
     // reading tile t and t-1 (the explicit vmcnt(0) before every barrier is what makes that true).
     auto iterate = [&](int t, const lds_char* __restrict__ kb, const lds_char* __restrict__ vb) {
-        step(yes{}, yes{}, t * T::BC + T::BC > wave_full_end, t, kb, vb);
+        step(yes{}, yes{}, no{}, t, kb, vb);
+        retire(t);
+    };
+    // Tiles [0, full_tiles) of this wave need no mask; [full_tiles, wave_tiles) are the diagonal or ragged ones.
+    const int full_tiles = min(wave_tiles, wave_full_end / T::BC);
+    auto iterate_masked = [&](int t, const lds_char* __restrict__ kb, const lds_char* __restrict__ vb) {
+        step(yes{}, yes{}, yes{}, t, kb, vb);
         retire(t);
     };
     int t = 0;
     if (ntiles > 0) {
-        if (wave_tiles > 0) step(yes{}, no{}, T::BC > wave_full_end, 0, kbuf_of(0), vbuf_of(2));
+        if (wave_tiles > 0) {
+            if (full_tiles > 0) step(yes{}, no{}, no{}, 0, kbuf_of(0), vbuf_of(2));
+            else step(yes{}, no{}, yes{}, 0, kbuf_of(0), vbuf_of(2));
+        }
         retire(0);
-        for (t = 1; t < wave_tiles; ++t) iterate(t, kbuf_of(t), vbuf_of(t - 1));
-        if (wave_tiles > 0) step(no{}, yes{}, false, t, kbuf_of(t), vbuf_of(t - 1));   // P.V of the last tile
+        for (t = 1; t < full_tiles; ++t) iterate(t, kbuf_of(t), vbuf_of(t - 1));
+        for (t = max(t, 1); t < wave_tiles; ++t) iterate_masked(t, kbuf_of(t), vbuf_of(t - 1));
+        if (wave_tiles > 0) step(no{}, yes{}, no{}, t, kbuf_of(t), vbuf_of(t - 1));   // P.V of the last tile
         for (t = max(t, 1); t < ntiles; ++t) retire(t);
     }
 
