@@ -44,8 +44,10 @@ def merge_bytes(w) -> float:
 
 
 def cpu_baseline(w, seconds: float):
-    """Time the fp64 oracle (blockwise form, key blocks of 1024, row blocks of 256) on a bounded sample:
-    row blocks of head (0,0) against all keys, run on a thread pool with one BLAS thread per worker."""
+    """Time the fp64 oracle (blockwise form, key blocks of 1024, row blocks of 256) on a bounded sample of
+    the workload: about `seconds` of wall time of (head, row block) pairs spread over the heads and over
+    each head's query range, every block against all of its keys, on a thread pool with one BLAS thread
+    per worker.  Input generation is outside the timed region."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
@@ -55,37 +57,74 @@ def cpu_baseline(w, seconds: float):
     import workloads as W
 
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
-    k = W.head_f64(w, W.K_T, 0, 0)
-    v = W.head_f64(w, W.V_T, 0, 0)
-    q = W.head_f64(w, W.Q_T, 0, 0)
     rb = 256
     starts = list(range(0, w.N_q, rb))
-    # probe one block to size the sample to about `seconds` of wall time
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    cache = {}
+
+    def head(i):
+        if i not in cache:
+            b, h = heads[i]
+            cache[i] = tuple(W.head_f64(w, t, b, h) for t in (W.Q_T, W.K_T, W.V_T))
+        return cache[i]
+
+    def run(job):
+        i, s = job
+        q, k, v = head(i)
+        rows = np.arange(s, min(s + rb, w.N_q))
+        oracle.blockwise_head(q[rows], k, v, w.scale, w.causal, w.offset, rows, 1024)
+        return rows
+
     with threadpool_limits(limits=1, user_api="blas"):
+        # probe one block (a late one: causal rows there see the most keys) to size the sample
+        probe_start = starts[-1]
         t0 = time.perf_counter()
-        oracle.blockwise_head(q[:rb], k, v, w.scale, w.causal, w.offset, np.arange(rb), 1024)
+        run((0, probe_start))
         one = time.perf_counter() - t0
-        nblk = int(max(1, min(len(starts), round(seconds / one * workers))))
-        # spread the sampled blocks evenly over the query range (causal rows differ in cost)
-        pick = [starts[int(i * len(starts) / nblk)] for i in range(nblk)]
-
-        def run(s):
-            rows = np.arange(s, min(s + rb, w.N_q))
-            oracle.blockwise_head(q[rows], k, v, w.scale, w.causal, w.offset, rows, 1024)
-            return rows
-
+        nblk = int(max(1, min(len(starts) * len(heads), round(seconds / one * workers))))
+        nheads = min(len(heads), -(-nblk // len(starts)))
+        per_head = -(-nblk // nheads)
+        hsel = [int(j * len(heads) / nheads) for j in range(nheads)]
+        jobs = [(i, starts[int(j * len(starts) / per_head)]) for i in hsel for j in range(per_head)]
+        for i in hsel:
+            head(i)
         t0 = time.perf_counter()
         with ThreadPoolExecutor(workers) as ex:
-            done = list(ex.map(run, pick))
+            done = list(ex.map(run, jobs))
         dt = time.perf_counter() - t0
     rows = np.concatenate(done)
     vis = np.minimum(w.N_kv, rows + w.offset + 1) if w.causal else np.full(len(rows), w.N_kv)
     flops = 4.0 * w.d * float(vis.sum())
     return {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
-        "sample": f"fp64 blockwise oracle, head (0,0), {len(rows)} query rows in {nblk} blocks of {rb} spread over "
-                  f"the {w.N_q} rows, each against all {w.N_kv} keys ({flops:.3e} FLOP in {dt:.1f} s)",
+        "sample": f"fp64 blockwise oracle (single pass, key blocks of 1024) on {len(jobs)} blocks of {rb} query "
+                  f"rows: {per_head} blocks spread over the {w.N_q} rows of each of {nheads} of the {len(heads)} "
+                  f"heads, each row against all of its visible keys of the {w.N_kv}; {flops:.3e} FLOP in {dt:.1f} s",
     }
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_traffic.txt")
+FWD_SOURCE = os.path.join(ROOT, "exact_blockwise_attention_fwd_amd", "csrc", "attn_fwd_bf16.hip")
+
+
+def recorded_traffic(w):
+    """HBM bytes per forward launch from the counter summary under profiles/ (FETCH_SIZE and WRITE_SIZE,
+    each scaled by what the counter reads for a plain copy of known size), or None when that summary is
+    missing, covers another workload, or was taken on a different forward-kernel source."""
+    import hashlib
+
+    try:
+        fields = {}
+        for line in open(TRAFFIC_FILE):
+            if ":" in line and not line.startswith((" ", "#", "|")):
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+        sha = hashlib.sha256(open(FWD_SOURCE, "rb").read()).hexdigest()
+        if fields.get("kernel_source_sha256") != sha or fields.get("workload") != w.name:
+            return None
+        return float(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def main():
@@ -95,7 +134,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ring_share_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (practical HBM ceiling; also the "
                          "reference size for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -199,7 +238,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": None if fwd_tflops is None else round(fwd_tflops, 2),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": None if fwd_tflops is None else round(fwd_tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": recorded_traffic(w)},
         "cpu_baseline": None,
     }
     if w.dtype != "bf16":

@@ -7,10 +7,9 @@
 // Attention", section 3, Transform stage) is bottom-right aligned; tiles wholly in the future are skipped.
 //
 // Mapping to CDNA4 (gfx950), designed for this chip rather than taken from the pages' GPU:
-//  * A workgroup is 4 wave64s.  Each wave owns QB blocks of 32 query rows of one (b, h): QB = 2 for d = 128
-//    (one wave per SIMD, ~360 registers with the output accumulators in AGPRs), QB = 1 for d = 64.  Every
-//    K or V operand read from LDS feeds QB MFMAs, which is what keeps LDS bandwidth (the transpose read
-//    below runs at half the rate of a plain 16-byte read) off the critical path at d = 128.
+//  * A workgroup is 4 wave64s, each owning 32 query rows of one (b, h); two workgroups share a CU, so
+//    every SIMD runs two waves whose softmax and matrix work interleave.  Key tiles are 64 keys for
+//    d = 128 and 128 keys for d = 64 (16 KiB of K and of V per tile either way).
 //  * Everything is computed transposed.  S^T = K Q^T uses v_mfma_f32_32x32x16_bf16 with A = K rows from
 //    LDS and B = Q^T held in registers for the whole key loop.  In the 32x32 accumulator layout a lane then
 //    holds 16 keys of ONE query (lane l and l^32 share query l%32), so the row max and row sum are in-lane
@@ -35,11 +34,13 @@
 //    whole iteration to land.
 //  * LDS rows are XOR-swizzled in 16-byte units so that the operand reads of each 16-lane block (K rows for
 //    S^T, four V rows for the transpose read) hit distinct banks.
-//  * exp is v_exp_f32 (base 2) with scale*log2(e) folded into one FMA per score.  The running max used as
-//    the exponent reference is only moved when some row of the wave has grown by more than 2^8 (in exp2
-//    units); until then the stale reference bounds every weight by 2^8, which fp32 sums and bf16 weights
-//    carry without loss, and the final division by the denominator accumulated against the same reference
-//    returns the same result.  Rescaling the output accumulator therefore becomes rare.
+//  * exp is v_exp_f32 (base 2) with scale*log2(e) folded into one FMA per score.  The exponent reference
+//    need not be the running max: weights are taken against the current reference, and only when a row
+//    has no reference yet or some row's weight sum for the tile exceeds 2^64 is the tile redone against
+//    its true max (which then becomes the reference, and the output is rescaled once).  Every weight is
+//    then at most 2^64, the fp32 sums stay far from overflow, and the single final division by the
+//    denominator accumulated against the same reference gives the running-max result up to rounding.
+//    The common path therefore has no row max, no rescale factor and no rescale of the accumulators.
 //  * Workgroup ids are remapped so that consecutive logical tiles (same head, neighbouring query rows,
 //    hence the same K/V stream) land on the same XCD and share its L2; causal launches start with the
 //    longest query tiles.
