@@ -78,7 +78,7 @@ struct Tile {
     static constexpr int QB = 1;      // 32-row query blocks per wave
     static constexpr int NW = 4;                     // waves per workgroup
     static constexpr int THREADS = 64 * NW;
-    static constexpr int WAVES_PER_SIMD = QB == 2 ? 1 : 2;
+    static constexpr int WAVES_PER_SIMD = 2;
     static constexpr int BR = 32 * QB * NW;          // query rows per workgroup
     static constexpr int BC = D == 128 ? 64 : 128;   // keys per tile
     static constexpr int NKB = BC / 32;              // 32-key blocks of S^T per tile
@@ -90,7 +90,10 @@ struct Tile {
     static constexpr int SEGS_PER_WAVE = SEGS / NW;
     static constexpr int RPS = 1024 / ROW;           // rows per segment
     static constexpr int LPR = ROW / 16;             // lanes (16-byte chunks) per row
-    static constexpr int LDS = 5 * TILE;             // K double-buffered, then V triple-buffered
+    static constexpr int L = 2;                      // tiles of lookahead: tile t+L is loaded when iteration t ends
+    static constexpr int NK = L, NV = L + 1;         // K and V buffers (V_{t-1} is still read in iteration t)
+    static constexpr int LPT = 2 * SEGS_PER_WAVE;
+    static constexpr int LDS = (NK + NV) * TILE;
     static_assert(SEGS % NW == 0, "segments split evenly over the waves");
     static_assert(NW * RPS * ROW == 4096, "a wave's load segments are 4 KiB apart");
 };
@@ -121,6 +124,17 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
 }
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// Workgroup barrier ordering LDS accesses only: this wave's LDS reads have returned (lgkmcnt(0)) before it
+// arrives.  Tile loads into LDS that are still in flight are not waited for here (a release fence would
+// wait for all of them); callers wait with an explicit vmcnt for exactly the loads that must have landed.
+// The empty asm statements keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
 
 template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd_bf16_kernel(FwdArgs a, int num_qt,
@@ -177,8 +191,8 @@ __global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd
         v_voff = r0 * T::ROW + 16 * (p ^ v_swz<D>(r0));
     }
     auto issue_tile = [&](int t) {
-        lds_char* kbuf = lds + (t & 1) * T::TILE;
-        lds_char* vbuf = lds + 2 * T::TILE + (t % 3) * T::TILE;
+        lds_char* kbuf = lds + (t % T::NK) * T::TILE;
+        lds_char* vbuf = lds + (T::NK + t % T::NV) * T::TILE;
         const long long base = (long long)t * T::TILE;
         const int left = (int)(kv_bytes - base);
         const __amdgpu_buffer_rsrc_t krs =
@@ -268,17 +282,12 @@ __global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd
         // Per-lane LDS offsets pass through an empty statement here, so that the compiler forms
         // "buffer + offset" once per step and folds the (kb, ks) constants into the instructions' offset
         // fields, instead of hoisting every offset+constant combination out of the loop.
-        int kro[T::NKS], vro[T::NDB];
 #pragma unroll
-        for (int ks = 0; ks < T::NKS; ++ks) {
-            kro[ks] = k_roff[ks];
-            __asm__ volatile("" : "+v"(kro[ks]));
-        }
+        for (int ks = 0; ks < T::NKS; ++ks) __asm__ volatile("" : "+v"(k_roff[ks]));
 #pragma unroll
-        for (int db = 0; db < T::NDB; ++db) {
-            vro[db] = v_roff[db];
-            __asm__ volatile("" : "+v"(vro[db]));
-        }
+        for (int db = 0; db < T::NDB; ++db) __asm__ volatile("" : "+v"(v_roff[db]));
+        const int (&kro)[T::NKS] = k_roff;
+        const int (&vro)[T::NDB] = v_roff;
         if (moved_prev) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
@@ -409,25 +418,27 @@ __global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd
     using yes = std::integral_constant<bool, true>;
     using no = std::integral_constant<bool, false>;
 
-    if (ntiles > 0) issue_tile(0);
-    if (ntiles > 1) issue_tile(1);
-    if (ntiles > 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * T::SEGS_PER_WAVE));   // vmcnt(tile-1 loads)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                                         // vmcnt(0)
-    __syncthreads();
+    // prologue: tiles 0 .. L-1 in flight, tile 0 must have landed (in every wave) before the first step
+    for (int t0 = 0; t0 < T::L && t0 < ntiles; ++t0) issue_tile(t0);
+    if (ntiles >= T::L) __builtin_amdgcn_s_waitcnt(0x0F70 | ((T::L - 1) * T::LPT));
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    lds_barrier();
 
-    // Every wave's loads of tile t+1 have landed and every wave is done with K_t and V_{t-1} after the
-    // barrier at the end of iteration t, so tile t+2 may then be loaded into their buffers.  All waves run
-    // exactly ntiles such barriers, whether or not they still have tiles to compute.
+    // End of iteration t: this wave's loads of tile t+1 have landed (tiles t+2 .. t+L-1 may still fly) and,
+    // after the barrier, every wave's have, and every wave is done with K_t and V_{t-1}; tile t+L is then
+    // loaded into their buffers.  All waves run exactly ntiles such barriers, whether or not they still have
+    // tiles to compute.
     auto retire = [&](int t) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-        __syncthreads();
-        if (t + 2 < ntiles) issue_tile(t + 2);
+        if (t + T::L - 1 < ntiles) __builtin_amdgcn_s_waitcnt(0x0F70 | ((T::L - 2) * T::LPT));
+        else __builtin_amdgcn_s_waitcnt(0x0F70);
+        lds_barrier();
+        if (t + T::L < ntiles) issue_tile(t + T::L);
     };
-    auto kbuf_of = [&](int t) { return (const lds_char*)(lds + (t & 1) * T::TILE); };
-    auto vbuf_of = [&](int t) { return (const lds_char*)(lds + 2 * T::TILE + (t % 3) * T::TILE); };
+    auto kbuf_of = [&](int t) { return (const lds_char*)(lds + (t % T::NK) * T::TILE); };
+    auto vbuf_of = [&](int t) { return (const lds_char*)(lds + (T::NK + t % T::NV) * T::TILE); };
     // The steady-state iteration gets its buffers as restrict-qualified pointers, distinct from those the
-    // loads issued by retire() write (tile t+2), so the compiler does not wait for those loads before
-    // reading tile t and t-1 (the explicit vmcnt(0) before every barrier is what makes that true).
+    // loads issued by retire() write (tile t+L), so the compiler does not wait for those loads before
+    // reading tile t and t-1 (the explicit vmcnt wait before every barrier is what makes that true).
     auto iterate = [&](int t, const lds_char* __restrict__ kb, const lds_char* __restrict__ vb) {
         step(yes{}, yes{}, no{}, t, kb, vb);
         retire(t);
@@ -441,8 +452,8 @@ __global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd
     int t = 0;
     if (ntiles > 0) {
         if (wave_tiles > 0) {
-            if (full_tiles > 0) step(yes{}, no{}, no{}, 0, kbuf_of(0), vbuf_of(2));
-            else step(yes{}, no{}, yes{}, 0, kbuf_of(0), vbuf_of(2));
+            if (full_tiles > 0) step(yes{}, no{}, no{}, 0, kbuf_of(0), vbuf_of(T::NV - 1));
+            else step(yes{}, no{}, yes{}, 0, kbuf_of(0), vbuf_of(T::NV - 1));
         }
         retire(0);
         for (t = 1; t < full_tiles; ++t) iterate(t, kbuf_of(t), vbuf_of(t - 1));
