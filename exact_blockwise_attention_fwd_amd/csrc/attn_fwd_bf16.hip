@@ -7,9 +7,10 @@
 // Attention", section 3, Transform stage) is bottom-right aligned; tiles wholly in the future are skipped.
 //
 // Mapping to CDNA4 (gfx950), designed for this chip rather than taken from the pages' GPU:
-//  * A workgroup is 4 wave64s, each owning 32 query rows of one (b, h); two workgroups share a CU, so
-//    every SIMD runs two waves whose softmax and matrix work interleave.  Key tiles are 64 keys for
-//    d = 128 and 128 keys for d = 64 (16 KiB of K and of V per tile either way).
+//  * Every wave owns 32 query rows of one (b, h), and every SIMD runs two waves.  Key tiles are 64 keys
+//    for d = 128 and 128 keys for d = 64 (16 KiB of K and of V per tile either way).  Two kernels share
+//    the machinery below and differ in their software pipeline: fwd_bf16_kernel (used for d = 64) and
+//    fwd_p3_kernel (d = 128), described where each is defined.
 //  * Everything is computed transposed.  S^T = K Q^T uses v_mfma_f32_32x32x16_bf16 with A = K rows from
 //    LDS and B = Q^T held in registers for the whole key loop.  In the 32x32 accumulator layout a lane then
 //    holds 16 keys of ONE query (lane l and l^32 share query l%32), so the row max and row sum are in-lane
@@ -27,11 +28,6 @@
 //    store instructions, and loads past the last key return zeros (the buffer resource's bound).  Each
 //    wave instruction fills one contiguous 1 KiB LDS segment in lane order, so the XOR swizzle of the LDS
 //    layout is applied by choosing which 16-byte global chunk each lane fetches.
-//  * K is double-buffered and V triple-buffered.  Iteration t computes S(t) and the weights of tile t, and
-//    the P.V product of tile t-1 (software pipelining: the softmax of one tile shares a basic block with
-//    the P.V MFMAs of the previous one, so the VALU and the matrix cores overlap inside one wave).  After
-//    the barrier that ends iteration t, tile t+2 is loaded into the buffers of K_t and V_{t-1}; it has a
-//    whole iteration to land.
 //  * LDS rows are XOR-swizzled in 16-byte units so that the operand reads of each 16-lane block (K rows for
 //    S^T, four V rows for the transpose read) hit distinct banks.
 //  * exp is v_exp_f32 (base 2) with scale*log2(e) folded into one FMA per score.  The exponent reference
@@ -47,6 +43,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <type_traits>
 
@@ -136,6 +133,11 @@ __device__ __forceinline__ void lds_barrier() {
     __asm__ volatile("" ::: "memory");
 }
 
+// ---- Two-stage pipeline (used for d = 64): workgroups of four waves (128 query rows), two per CU.  K is
+// double-buffered and V triple-buffered.  Iteration t computes S(t) and the weights of tile t, and the P.V
+// product of tile t-1: the softmax of one tile shares a basic block with the P.V MFMAs of the previous one,
+// so the VALU and the matrix cores overlap inside one wave.  After the barrier that ends iteration t, tile
+// t+2 is loaded into the buffers of K_t and V_{t-1}; it has a whole iteration to land.
 template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd_bf16_kernel(FwdArgs a, int num_qt,
                                                                                             int total, int per_xcd) {
@@ -519,13 +521,429 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// ---- d = 128: three-stage software pipeline with a fixed interleave.
+//
+// Step t of a wave computes the softmax of tile t, whose scores S(t) were produced by the previous step,
+// next to two batches of MFMAs that do not depend on it:
+//   part 1:  P.V of tile t-1 (16 MFMAs, V^T by transpose reads)      with the scaling and exp of tile t's scores
+//   part 2:  S(t+1) = K_{t+1} Q^T (16 MFMAs)                          with the row sums and bf16 packs of tile t
+// so every VALU instruction of a step has an MFMA of the same step to hide under, and the order (two MFMAs,
+// a share of the VALU work, the LDS reads for two MFMAs ahead) is pinned with scheduling fences.  Scores
+// and weights need no double buffers: part 1 reads the scores before part 2 overwrites them, and part 2
+// writes the new weights after part 1's MFMAs have read the old ones.  The rare redo of a tile (see the
+// exponent reference rule in the file header) recomputes its scores from K_t, which stays in LDS until
+// the step ends.  Two waves share every SIMD.  A workgroup is either four waves (128 query rows) or eight
+// (256 rows: both waves of each SIMD then belong to it and share its K/V tiles, and with one workgroup per
+// CU the LDS holds three steps of lead for every load).  K_{t+NK} and V_{t+NV-1} are loaded when step t ends.
+template <int NW_>
+struct P3 {
+    static constexpr int D = 128, NW = NW_, THREADS = 64 * NW, BR = 32 * NW, BC = 64;
+    static constexpr int NKB = BC / 32, NDB = D / 32, NKS = D / 16, ROW = 2 * D, TILE = BC * ROW;
+    static constexpr int SEGS = TILE / 1024, SEGS_PER_WAVE = SEGS / NW;
+    static constexpr int RPS = 1024 / ROW, LPR = ROW / 16;
+    static constexpr int L = NW == 8 ? 3 : 1;        // steps of lead for every tile load
+    static constexpr int NK = L + 2, NV = L + 1;     // K and V buffers
+    static constexpr int LDS = (NK + NV) * TILE;
+    static constexpr int WSTRIDE = NW * RPS * ROW;   // bytes between the load segments of one wave
+    static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
+};
+
+template <int NW, bool CAUSAL, bool OUT_F32>
+__global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, int num_qt, int total, int per_xcd) {
+    using T = P3<NW>;
+    constexpr int D = T::D;
+    constexpr int WS = T::WSTRIDE;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    lds_char* const lds = (lds_char*)smem;
+
+    const int w_hw = blockIdx.x;
+    const int logical = (w_hw % NXCD) * per_xcd + w_hw / NXCD;
+    if (logical >= total) return;
+    const int bh = logical / num_qt;
+    int qt = logical % num_qt;
+    if (CAUSAL) qt = num_qt - 1 - qt;                // longest query tiles first
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5;
+    const int col = lane & 31;
+    const int q0 = qt * T::BR;
+    const int qw0 = q0 + 32 * wave;
+
+    const uint16_t* qh = static_cast<const uint16_t*>(a.q) + (size_t)bh * a.q_head_stride;
+    const uint16_t* kh = static_cast<const uint16_t*>(a.k) + (size_t)bh * a.kv_head_stride;
+    const uint16_t* vh = static_cast<const uint16_t*>(a.v) + (size_t)bh * a.kv_head_stride;
+
+    const int q_last = min(q0 + T::BR, a.n_q) - 1;
+    int kv_end = a.n_kv;
+    if (CAUSAL) kv_end = max(0, min(a.n_kv, q_last + a.offset + 1));
+    const int ntiles = (kv_end + T::BC - 1) / T::BC;
+    const int qw_last = min(qw0 + 31, a.n_q - 1);
+    const int wave_key_end = qw0 >= a.n_q ? 0 : CAUSAL ? min(kv_end, qw_last + a.offset + 1) : kv_end;
+    const int wave_full_end = CAUSAL ? min(a.n_kv, qw0 + a.offset + 1) : a.n_kv;
+    const int wave_tiles = min(ntiles, (wave_key_end + T::BC - 1) / T::BC);
+    const int full_tiles = min(wave_tiles, wave_full_end / T::BC);
+
+    // ---- global -> LDS loads (buffer loads straight into LDS; past the last key they return zeros)
+    const long long kv_bytes = (long long)a.n_kv * T::ROW;
+    int k_voff, v_voff;
+    {
+        const int r0 = T::RPS * wave + lane / T::LPR;
+        const int p = lane % T::LPR;
+        k_voff = r0 * T::ROW + 16 * (p ^ k_swz<D>(r0));
+        v_voff = r0 * T::ROW + 16 * (p ^ v_swz<D>(r0));
+    }
+    auto load_k = [&](int j) __attribute__((always_inline)) {   // K_j into K buffer j % NK
+        if (j >= ntiles) return;
+        lds_char* buf = lds + (j % T::NK) * T::TILE;
+        const long long base = (long long)j * T::TILE;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)kh + base), (short)0, (int)(kv_bytes - base), BUF_RSRC_WORD3);
+#pragma unroll
+        for (int k = 0; k < T::SEGS_PER_WAVE; ++k)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (wave + T::NW * k) * 1024), 16, k_voff + WS * k, 0, 0, 0);
+    };
+    auto load_v = [&](int j) __attribute__((always_inline)) {   // V_j into V buffer j % NV
+        if (j >= ntiles) return;
+        lds_char* buf = lds + (T::NK + (j % T::NV)) * T::TILE;
+        const long long base = (long long)j * T::TILE;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)vh + base), (short)0, (int)(kv_bytes - base), BUF_RSRC_WORD3);
+#pragma unroll
+        for (int k = 0; k < T::SEGS_PER_WAVE; ++k)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (wave + T::NW * k) * 1024), 16, v_voff + WS * k, 0, 0, 0);
+    };
+    auto kbuf_of = [&](int j) __attribute__((always_inline)) { return (const lds_char*)(lds + (j % T::NK) * T::TILE); };
+    auto vbuf_of = [&](int j) __attribute__((always_inline)) { return (const lds_char*)(lds + (T::NK + (j % T::NV)) * T::TILE); };
+
+    // ---- Q^T fragments (B operand), held for the whole key loop
+    const float scale_abs = fabsf(a.scale);
+    const unsigned neg = a.scale < 0.f ? 0x80008000u : 0u;
+    const unsigned keep = a.scale == 0.f ? 0u : 0xffffffffu;
+    bf16x8 qf[T::NKS];
+    {
+        const int qi = qw0 + col;
+#pragma unroll
+        for (int ks = 0; ks < T::NKS; ++ks) {
+            u32x4 x = qi < a.n_q ? *reinterpret_cast<const u32x4*>(qh + (size_t)qi * D + 16 * ks + 8 * h)
+                                 : u32x4{0, 0, 0, 0};
+            x = (x ^ neg) & keep;
+            qf[ks] = as_bf16x8(x);
+        }
+    }
+    const float c = a.scale == 0.f ? LOG2E : scale_abs * LOG2E;
+
+    const int kslot = swap23(col);
+    int k_roff[T::NKS];
+#pragma unroll
+    for (int ks = 0; ks < T::NKS; ++ks) k_roff[ks] = kslot * T::ROW + 16 * ((2 * ks + h) ^ k_swz<D>(kslot));
+    int v_roff[T::NDB];
+    {
+        const int b = lane >> 4, j = lane & 15, e = j >> 2, s4 = j & 3, dp = b & 1;
+#pragma unroll
+        for (int db = 0; db < T::NDB; ++db) {
+            const int chunk = 4 * db + 2 * dp + (s4 >> 1);
+            v_roff[db] = (8 * h + e) * T::ROW + 16 * (chunk ^ v_swz<D>(e)) + 8 * (s4 & 1);
+        }
+    }
+
+    f32x16 acc[T::NDB];
+#pragma unroll
+    for (int db = 0; db < T::NDB; ++db) acc[db] = f32x16{};
+    float m = -INFINITY, l = 0.f, alpha_prev = 1.f;
+    bool moved = false;
+    f32x16 s[T::NKB];           // scores of the tile whose softmax is next
+    u32x4 p[T::NKB][2];         // bf16 weights of the tile whose P.V is next
+
+    auto s_all = [&](f32x16 (&sc)[T::NKB], const lds_char* kbuf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < T::NKB; ++kb) sc[kb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < T::NKS; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < T::NKB; ++kb) {
+                const u32x4 kv = *(const lds_u32x4*)(kbuf + k_roff[ks] + 32 * kb * T::ROW);
+                sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qf[ks], sc[kb], 0, 0, 0);
+            }
+    };
+    auto mask_tile = [&](int t, f32x16 (&sc)[T::NKB]) __attribute__((always_inline)) {
+        const int kt = t * T::BC;
+        const int qi = qw0 + col;
+        const int lim = CAUSAL ? min(a.n_kv - 1, qi + a.offset) : a.n_kv - 1;
+#pragma unroll
+        for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int key = kt + 32 * kb + 16 * (j >> 3) + 8 * h + (j & 7);
+                if (key > lim) sc[kb][j] = -INFINITY;
+            }
+    };
+    // weights and their row sum against reference mc (the plain form, used by the rare redo)
+    auto weights = [&](const f32x16 (&sc)[T::NKB], float mc) __attribute__((always_inline)) {
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < T::NKB; ++kb) {
+            float e[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][j], c, -mc));
+            float r8[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) r8[j] = e[2 * j] + e[2 * j + 1];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) r8[j] = r8[2 * j] + r8[2 * j + 1];
+            rs += (r8[0] + r8[1]) + (r8[2] + r8[3]);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) p[kb][ks][w] = pack_bf16(e[8 * ks + 2 * w], e[8 * ks + 2 * w + 1]);
+        }
+        return rs;
+    };
+
+    // One step t (see the header of this kernel).  kn = K_{t+1}, kc = K_t, vp = V_{t-1}, as restrict-qualified
+    // pointers distinct from the buffers the loads issued at the step's end write (K_{t+NK}, V_{t+NV-1}), so
+    // the compiler does not wait for those loads before reading; the explicit vmcnt wait before every
+    // barrier is what makes that true.
+    auto step = [&](auto do_soft, auto do_pv, auto do_s, int t, const lds_char* __restrict__ kn,
+                    const lds_char* __restrict__ kc, const lds_char* __restrict__ vp) __attribute__((always_inline)) {
+        constexpr bool SOFT = decltype(do_soft)::value, PV = decltype(do_pv)::value, S = decltype(do_s)::value;
+        // a reference moved by the previous softmax: rescale the output before P.V(t-1) adds to it
+        if (moved) {
+#pragma unroll
+            for (int db = 0; db < T::NDB; ++db) acc[db] *= alpha_prev;
+            moved = false;
+        }
+        if constexpr (SOFT) {
+            if (t >= full_tiles) mask_tile(t, s);   // diagonal and ragged tiles
+        }
+        const bool none = m == -INFINITY;
+        const float mc = none ? 0.f : m * c;
+        float e[2 * 16];
+        // ---- part 1: P.V(t-1) (two transpose reads per MFMA, two MFMAs ahead) with the exps of tile t
+        {
+            i16x4 vl[16], vhh[16];
+            auto vread = [&](int i) __attribute__((always_inline)) {
+                const int kb = i >> 3, ks = (i >> 2) & 1, db = i & 3;
+                const lds_char* q = vp + v_roff[db] + (32 * kb + 16 * ks) * T::ROW;
+                vl[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)q);
+                vhh[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q + 4 * T::ROW));
+            };
+            if constexpr (PV) {
+                vread(0);
+                vread(1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if constexpr (PV) {
+                    if (i + 2 < 16) vread(i + 2);
+                    const int kb = i >> 3, ks = (i >> 2) & 1, db = i & 3;
+                    const u32x4 vv = {__builtin_bit_cast(u32x2, vl[i])[0], __builtin_bit_cast(u32x2, vl[i])[1],
+                                      __builtin_bit_cast(u32x2, vhh[i])[0], __builtin_bit_cast(u32x2, vhh[i])[1]};
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), as_bf16x8(p[kb][ks]), acc[db], 0, 0, 0);
+                }
+                if constexpr (SOFT) {
+                    e[2 * i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i >> 3][(2 * i) & 15], c, -mc));
+                    e[2 * i + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i >> 3][(2 * i + 1) & 15], c, -mc));
+                }
+                if constexpr (PV) __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // ---- part 2: S(t+1) (one K read per MFMA, two MFMAs ahead) with the sums and packs of tile t
+        float r[16];
+        {
+            u32x4 kv[16];
+            auto kread = [&](int i) __attribute__((always_inline)) {
+                kv[i] = *(const lds_u32x4*)(kn + k_roff[i >> 1] + 32 * (i & 1) * T::ROW);
+            };
+            if constexpr (S) {
+                kread(0);
+                kread(1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if constexpr (S) {
+                    if (i + 2 < 16) kread(i + 2);
+                    const int ks = i >> 1, kb = i & 1;
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv[i]), qf[ks], ks == 0 ? f32x16{} : s[kb], 0, 0, 0);
+                }
+                if constexpr (SOFT) {
+                    r[i] = e[2 * i] + e[2 * i + 1];
+                    p[i >> 3][(i >> 2) & 1][i & 3] = pack_bf16(e[2 * i], e[2 * i + 1]);
+                    __asm__ volatile("" ::"v"(p[i >> 3][(i >> 2) & 1][i & 3]));   // keep the pack in this slot
+                }
+                if constexpr (S) __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if constexpr (SOFT) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) r[j] = r[2 * j] + r[2 * j + 1];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) r[j] = r[2 * j] + r[2 * j + 1];
+            float rs = (r[0] + r[1]) + (r[2] + r[3]);
+            float alpha = 1.f;
+            if (__any(none || !(rs <= REF_BOUND))) {
+                // rare: no reference yet, or a weight sum above 2^64.  Tile t's scores were replaced by
+                // S(t+1) (when there was one): recompute them from K_t, mask, and redo the tile against its max.
+                f32x16 sc[T::NKB];
+                if constexpr (S) {
+                    s_all(sc, kc);
+                    if (t >= full_tiles) mask_tile(t, sc);
+                } else {
+#pragma unroll
+                    for (int kb = 0; kb < T::NKB; ++kb) sc[kb] = s[kb];
+                }
+                float mt = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) mt = fmaxf(mt, sc[kb][j]);
+                mt = fmaxf(mt, wave_xor32(mt));
+                const float m_new = fmaxf(m, mt);
+                alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * c);
+                if (__any(m != -INFINITY && m_new != m)) {
+                    alpha_prev = alpha;
+                    moved = true;
+                }
+                m = m_new;
+                rs = weights(sc, m_new == -INFINITY ? 0.f : m_new * c);
+            }
+            l = __builtin_fmaf(l, alpha, rs);
+        }
+    };
+    // End of step t: every wave's loads of K_{t+2} and V_t have landed and every wave is done with K_t and
+    // V_{t-1}; K_{t+NK} and V_{t+NV-1} then go into their buffers.  All waves run exactly ntiles such barriers.
+    auto retire = [&](int t) __attribute__((always_inline)) {
+        // K_{t+2} and V_t were issued L steps ago; the loads of the L-1 later retires may still fly (when
+        // all of them exist; near the end, wait for everything)
+        if (t + T::L + 1 < ntiles) __builtin_amdgcn_s_waitcnt(0x0F70 | ((T::L - 1) * 2 * T::SEGS_PER_WAVE));
+        else __builtin_amdgcn_s_waitcnt(0x0F70);
+        lds_barrier();
+        load_k(t + T::NK);
+        load_v(t + T::NV - 1);
+    };
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+
+    // ---- prologue: K_0, K_1, K_2 and V_0 in flight; all must land (in every wave) before S(0)
+    for (int j = 0; j < T::NK; ++j) load_k(j);
+    for (int j = 0; j < T::NV - 1; ++j) load_v(j);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    lds_barrier();
+
+    // Steps 0 .. nt-1 (step t: softmax of tile t, P.V of t-1, S of t+1), then the P.V of the last tile.
+    const int nt = wave_tiles;
+    int t = 0;
+    if (nt > 0) {
+        s_all(s, kbuf_of(0));
+        if (nt > 1) {
+            step(yes{}, no{}, yes{}, 0, kbuf_of(1), kbuf_of(0), vbuf_of(0));
+            retire(0);
+            for (t = 1; t < nt - 1; ++t) {
+                step(yes{}, yes{}, yes{}, t, kbuf_of(t + 1), kbuf_of(t), vbuf_of(t - 1));
+                retire(t);
+            }
+            step(yes{}, yes{}, no{}, t, kbuf_of(t), kbuf_of(t), vbuf_of(t - 1));   // no next S
+        } else {
+            step(yes{}, no{}, no{}, 0, kbuf_of(0), kbuf_of(0), vbuf_of(0));
+        }
+        // P.V of the last tile, after the barrier that ends its step: that barrier is what makes the last V
+        // tile visible (every wave waited for its loads of it), and it does not reload that V buffer
+        retire(t);
+        ++t;
+        step(no{}, yes{}, no{}, t, kbuf_of(t), kbuf_of(t), vbuf_of(nt - 1));
+    }
+    for (; t < ntiles; ++t) retire(t);   // the rest of the workgroup's barriers and loads
+
+    // ---- epilogue: one division by the final denominator; lse = scaled reference + ln(l)
+    {
+        const int qi = qw0 + col;
+        const float l_tot = l + wave_xor32(l);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        if (qi < a.n_q) {
+            if (OUT_F32) {
+                float* oh = static_cast<float*>(a.o) + (size_t)bh * a.q_head_stride + (size_t)qi * D;
+#pragma unroll
+                for (int db = 0; db < T::NDB; ++db)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x16& ac = acc[db];
+                        f32x4 o4 = {ac[4 * g] * inv, ac[4 * g + 1] * inv, ac[4 * g + 2] * inv, ac[4 * g + 3] * inv};
+                        *reinterpret_cast<f32x4*>(oh + 32 * db + 8 * g + 4 * h) = o4;
+                    }
+            } else {
+                uint16_t* oh = static_cast<uint16_t*>(a.o) + (size_t)bh * a.q_head_stride + (size_t)qi * D;
+#pragma unroll
+                for (int db = 0; db < T::NDB; ++db)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x16& ac = acc[db];
+                        u32x2 o2 = {pack_bf16(ac[4 * g] * inv, ac[4 * g + 1] * inv),
+                                    pack_bf16(ac[4 * g + 2] * inv, ac[4 * g + 3] * inv)};
+                        *reinterpret_cast<u32x2*>(oh + 32 * db + 8 * g + 4 * h) = o2;
+                    }
+            }
+            if (h == 0) a.lse[(size_t)bh * a.n_q + qi] = l_tot > 0.f ? m * scale_abs + logf(l_tot) : -INFINITY;
+        }
+    }
+}
+
+template <int NW, bool CAUSAL, bool OUT_F32>
+hipError_t launch_p3(const FwdArgs& a, hipStream_t st) {
+    using T = P3<NW>;
+    const int num_qt = (a.n_q + T::BR - 1) / T::BR;
+    const long long total_ll = (long long)num_qt * a.bh;
+    if (total_ll > 0x7fffffffLL - NXCD) return hipErrorInvalidValue;
+    if ((long long)a.n_kv * T::ROW > 0x7fffffffLL) return hipErrorInvalidValue;   // buffer bound is 31-bit
+    const int total = (int)total_ll;
+    const int per_xcd = (total + NXCD - 1) / NXCD;
+    const int grid = per_xcd * NXCD;
+    auto kern = fwd_p3_kernel<NW, CAUSAL, OUT_F32>;
+    static bool attr_set = false;   // LDS above the default limit needs an explicit opt-in
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(T::THREADS), T::LDS, st, a, num_qt, total, per_xcd);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+// Workgroup size of the d = 128 kernel: eight waves (256 query rows, one workgroup per CU) when the launch
+// has at least eight such workgroups per CU, four waves (128 rows, two workgroups per CU) otherwise, where
+// smaller workgroups balance better.  ATTN_BF16_D128_WAVES=4 or 8 forces one of them (used by the tests to
+// run every shape through both).
+static int d128_waves(const FwdArgs& a) {
+    if (const char* e = getenv("ATTN_BF16_D128_WAVES")) {
+        const int v = atoi(e);
+        if (v == 4 || v == 8) return v;
+    }
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cus[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    const long long wide = (long long)((a.n_q + 255) / 256) * a.bh;
+    return wide >= 8LL * cus[dev] ? 8 : 4;
+}
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, bool out_f32, hipStream_t s) {
     const bool c = a.causal != 0;
     if (a.d == 128) {
-        if (c) return out_f32 ? launch_t<128, true, true>(a, s) : launch_t<128, true, false>(a, s);
-        return out_f32 ? launch_t<128, false, true>(a, s) : launch_t<128, false, false>(a, s);
+        if (d128_waves(a) == 8) {
+            if (c) return out_f32 ? launch_p3<8, true, true>(a, s) : launch_p3<8, true, false>(a, s);
+            return out_f32 ? launch_p3<8, false, true>(a, s) : launch_p3<8, false, false>(a, s);
+        }
+        if (c) return out_f32 ? launch_p3<4, true, true>(a, s) : launch_p3<4, true, false>(a, s);
+        return out_f32 ? launch_p3<4, false, true>(a, s) : launch_p3<4, false, false>(a, s);
     }
     if (a.d == 64) {
         if (c) return out_f32 ? launch_t<64, true, true>(a, s) : launch_t<64, true, false>(a, s);

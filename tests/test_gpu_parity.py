@@ -114,6 +114,44 @@ def test_small_full(i):
         assert_parity(err, w.dtype, f"{w.name} chunks={P}")
 
 
+# The bf16 d = 128 kernel runs as four-wave (128-row) or eight-wave (256-row) workgroups, chosen by the
+# launch size; ATTN_BF16_D128_WAVES forces one.  Every shape below runs through both, against the oracle, and
+# the two must agree bit for bit (each row sees the same tiles in the same order either way).
+D128_SHAPES = [
+    # B, H, N_q, N_kv, causal
+    (1, 2, 300, 777, False),
+    (1, 2, 300, 777, True),
+    (2, 1, 333, 333, True),
+    (1, 1, 1000, 257, True),     # the first rows see no key
+    (1, 1, 257, 1000, True),
+    (1, 1, 700, 700, False),     # three 256-row workgroups, the last one ragged
+    (1, 2, 513, 1500, True),
+    (1, 1, 1, 64, False),
+    (1, 1, 64, 1, True),
+    (1, 1, 256, 4100, False),    # many tiles, then a ragged one
+]
+
+
+@pytest.mark.parametrize("case", D128_SHAPES, ids=lambda c: "x".join(map(str, c[:4])) + ("c" if c[4] else "n"))
+def test_d128_both_workgroup_sizes(case, monkeypatch):
+    B, H, N_q, N_kv, causal = case
+    w = W.Workload("d128wg", B, H, N_q, N_kv, 128, "bf16", causal, 1, seed=3000 + N_q + N_kv)
+    st, (q, k, v) = make(w)
+    o_ref, l_ref = oracle_full(st, w)
+    outs = {}
+    for waves in ("4", "8"):
+        monkeypatch.setenv("ATTN_BF16_D128_WAVES", waves)
+        o, lse = A.fwd(q, k, v, causal=causal, scale=w.scale)
+        o32, l32 = A.fwd_ex(q, k, v, causal=causal, scale=w.scale, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        err = errors(out_to_f64(o), out_to_f64(lse), o_ref, l_ref)
+        print(w, waves, err, flush=True)
+        assert_parity(err, "bf16", f"{w.name} waves={waves}")
+        outs[waves] = (o.cpu(), lse.cpu(), o32.cpu(), l32.cpu())
+    for a_, b_ in zip(outs["4"], outs["8"]):
+        assert torch.equal(a_, b_), "four- and eight-wave workgroups disagree"
+
+
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_unusual_scales(scale, dt):
