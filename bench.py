@@ -3,20 +3,24 @@
 
 One step = one pass of the whole path over one batch of seeded synthetic input: for the ring-share workload
 (B1 H32, 16384 local query rows against 131072 keys streamed as 8 chunks of 16384, bf16, d128, the last
-chunk causal) that is 8 forward launches into fp32 partials and 7 merges, the last writing bf16 O and
-the fp32 LSE.  Inputs are resident in HBM before the timed region.  Prints ONE JSON line.
+chunk causal) that is 8 forward launches, the first writing an fp32 partial and each later one folding its
+chunk into that partial in its epilogue (the last one writing bf16 O and the fp32 LSE).  Inputs are
+resident in HBM before the timed region.  Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 `value` is attention TFLOP/s of the whole step (algorithmic FLOPs: 4*d per visible query/key pair, a square
 causal block counted as N^2/2) over the step time.  The `roofline` object covers the dominant kernel (the
 forward launches), timed with HIP events that the library records on the stream the kernels run on.
-`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same workload on this host's cores.
+`merge` times attn_merge on its own, in place on fp32 partials of the workload's shape (the operation the
+chunked step fuses into its forward launches), against the HBM peak.  `cpu_baseline` times the fp64 CPU
+oracle on a bounded sample of the same workload on this host's cores.
 """
 from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -34,13 +38,38 @@ def log(msg):
 
 
 def merge_bytes(w) -> float:
-    """Algorithmic HBM bytes of the merges of one chunked step: per row, read two partial rows and lse
-    values, write one row and one lse.  All but the last merge are fp32 -> fp32; the last writes bf16."""
+    """Algorithmic HBM bytes of one fp32 -> fp32 merge of two partials of the workload's shape: per row, read
+    two partial rows and two lse values, write one row and one lse."""
     rows = w.B * w.H * w.N_q
-    n = w.chunks - 1
-    f32_merge = rows * (w.d * (4 + 4 + 4) + 12)
-    last = rows * (w.d * (4 + 4 + (2 if w.dtype == "bf16" else 4)) + 12)
-    return (n - 1) * f32_merge + last if n >= 1 else 0.0
+    return float(rows * (w.d * (4 + 4 + 4) + 12))
+
+
+def time_merge(w, reps: int):
+    """attn_merge in place on fp32 partials [B,H,N_q,d] (seeded values, the empty rows of a causal chunk
+    included), timed with the library's own launch events."""
+    import torch
+
+    import exact_blockwise_attention_fwd_amd as A
+
+    g = torch.Generator(device="cuda").manual_seed(w.seed)
+    shape = (w.B, w.H, w.N_q, w.d)
+    oa = torch.randn(shape, device="cuda", generator=g)
+    ob = torch.randn(shape, device="cuda", generator=g)
+    la = torch.randn(shape[:3], device="cuda", generator=g)
+    lb = torch.randn(shape[:3], device="cuda", generator=g)
+    lb[..., : w.N_q // 8] = -math.inf
+    for _ in range(2):
+        A.merge(oa, la, ob, lb, out=oa, lse=la)
+    torch.cuda.synchronize()
+    A.timing_enable(True)
+    A.timing_read()
+    for _ in range(reps):
+        A.merge(oa, la, ob, lb, out=oa, lse=la)
+    torch.cuda.synchronize()
+    A.timing_enable(False)
+    n, ms = A.timing_read()["merge"]
+    del oa, ob, la, lb
+    return ms / max(n, 1)
 
 
 def cpu_baseline(w, seconds: float):
@@ -218,10 +247,11 @@ def main():
     flops = w.flops()
     value = flops / (ms * 1e-3) / 1e12
     n_fwd, fwd_ms = kt["fwd"]
-    n_mrg, mrg_ms = kt["merge"]
     fwd_tflops = flops * args.steps / (fwd_ms * 1e-3) / 1e12 if fwd_ms > 0 else None
+    merge_ms = time_merge(w, 10)
     mb = merge_bytes(w)
-    merge_gbs = mb * args.steps / (mrg_ms * 1e-3) / 1e9 if mrg_ms > 0 else None
+    merge_gbs = mb / (merge_ms * 1e-3) / 1e9 if merge_ms > 0 else None
+    log(f"attn_merge alone: {merge_ms:.4f} ms, {merge_gbs:.1f} GB/s")
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -233,8 +263,9 @@ def main():
         "fwd_kernel": {"launches_per_step": n_fwd / args.steps, "ms_per_step": fwd_ms / args.steps,
                        "tflops": None if fwd_tflops is None else round(fwd_tflops, 2)},
         "merge": None if merge_gbs is None else {
-            "launches_per_step": n_mrg / args.steps, "ms_per_step": mrg_ms / args.steps,
-            "bytes_per_step": mb, "gbs": round(merge_gbs, 1), "pct_hbm_peak": round(100 * merge_gbs / HBM_PEAK_GBS, 2)},
+            "what": "attn_merge alone, fp32 partials in place, rows = B*H*N_q", "rows": w.B * w.H * w.N_q,
+            "ms": round(merge_ms, 4), "bytes": mb, "gbs": round(merge_gbs, 1),
+            "pct_hbm_peak": round(100 * merge_gbs / HBM_PEAK_GBS, 2)},
         "roofline": {"bound": "mfma", "achieved": None if fwd_tflops is None else round(fwd_tflops, 2),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": None if fwd_tflops is None else round(fwd_tflops / BF16_PEAK_TFLOPS, 4),

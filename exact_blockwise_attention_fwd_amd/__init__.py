@@ -8,6 +8,7 @@ streams.  If the library has not been built, every call raises (there is no fall
     o, lse = fwd(q, k, v, causal=True)                # q, k, v: [B, H, N, d] cuda tensors, bf16 or fp32
     o, lse = fwd_chunked(q, k, v, chunks=8, causal=True)
     o, lse = merge(o_a, lse_a, o_b, lse_b)
+    o, lse = fwd_acc(q, k, v, o_acc, lse_acc, causal_offset=..., key_range=(lo, hi))   # fold a key range in
 """
 from __future__ import annotations
 
@@ -42,6 +43,7 @@ def lib() -> ctypes.CDLL:
     vp, i, f, ll, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_longlong, ctypes.c_size_t
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     L.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, ll, ll, i, i, vp]
+    L.attn_fwd_acc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, ll, ll, i, i, vp]
     L.attn_merge.argtypes = [vp, vp, vp, vp, vp, vp, ll, i, i, i, vp]
     L.attn_fwd_chunked_workspace_bytes.argtypes = [i, i, i, i, i]
     L.attn_fwd_chunked_workspace_bytes.restype = sz
@@ -52,7 +54,7 @@ def lib() -> ctypes.CDLL:
     L.attn_last_error.restype = ctypes.c_char_p
     L.attn_timing_enable.argtypes = [i]
     L.attn_timing_read.argtypes = [ctypes.POINTER(ll), ctypes.POINTER(ctypes.c_double)]
-    for name in ("attn_fwd", "attn_fwd_ex", "attn_merge", "attn_fwd_chunked", "attn_timing_enable",
+    for name in ("attn_fwd", "attn_fwd_ex", "attn_fwd_acc", "attn_merge", "attn_fwd_chunked", "attn_timing_enable",
                  "attn_timing_read"):
         getattr(L, name).restype = i
     _lib = L
@@ -127,6 +129,37 @@ def fwd_ex(q, k, v, causal: bool = False, scale: float | None = None, causal_off
     _check(lib().attn_fwd_ex(q.data_ptr(), k.data_ptr() + lo * d * es, v.data_ptr() + lo * d * es,
                              out.data_ptr(), lse.data_ptr(), B, H, N_q, hi - lo, d, int(causal), scale,
                              offset, n_total * d, dt, odt, _stream(q)), "attn_fwd_ex")
+    return out, lse
+
+
+def fwd_acc(q, k, v, o_acc, lse_acc, causal: bool = False, scale: float | None = None,
+            causal_offset: int | None = None, key_range: tuple[int, int] | None = None, out_dtype=None,
+            out=None, lse=None):
+    """fwd_ex over keys [lo, hi) merged, in the kernel's epilogue, into the running fp32 partial
+    (o_acc, lse_acc).  With out=o_acc and lse=lse_acc (and an fp32 out_dtype) the fold is in place."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o_acc, "o_acc"), (lse_acc, "lse_acc")):
+        _need(t, n)
+    B, H, N_q, d = q.shape
+    if o_acc.dtype != torch.float32 or lse_acc.dtype != torch.float32:
+        raise TypeError("o_acc and lse_acc must be float32")
+    if tuple(o_acc.shape) != (B, H, N_q, d) or tuple(lse_acc.shape) != (B, H, N_q):
+        raise ValueError("o_acc must be [B, H, N_q, d] and lse_acc [B, H, N_q]")
+    n_total = k.shape[2]
+    lo, hi = key_range if key_range is not None else (0, n_total)
+    if not (0 <= lo <= hi <= n_total):
+        raise ValueError(f"key_range {key_range} outside [0, {n_total}]")
+    dt = _dtype_code(q)
+    odt = dt if out_dtype is None else _dtype_code(torch.empty(0, dtype=out_dtype))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    offset = (hi - lo) - N_q if causal_offset is None else int(causal_offset)
+    out = torch.empty((B, H, N_q, d), dtype=_torch_dtype(odt), device=q.device) if out is None else out
+    lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    es = q.element_size()
+    _check(lib().attn_fwd_acc(q.data_ptr(), k.data_ptr() + lo * d * es, v.data_ptr() + lo * d * es,
+                              o_acc.data_ptr(), lse_acc.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N_q,
+                              hi - lo, d, int(causal), scale, offset, n_total * d, dt, odt, _stream(q)),
+           "attn_fwd_acc")
     return out, lse
 
 

@@ -155,7 +155,7 @@ int clamp_offset(long long off, int N_q, int N_kv) {
 
 int launch_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q,
                int N_kv, int d, int causal, float scale, long long offset, long long kv_stride, int in_dtype,
-               int out_dtype, hipStream_t s) {
+               int out_dtype, hipStream_t s, const float* o_prev = nullptr, const float* lse_prev = nullptr) {
     attn::FwdArgs a;
     a.q = Q;
     a.k = K;
@@ -171,6 +171,8 @@ int launch_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
     a.causal = causal ? 1 : 0;
     a.offset = causal ? clamp_offset(offset, N_q, N_kv) : N_kv;
     a.scale = scale;
+    a.o_prev = o_prev;
+    a.lse_prev = lse_prev;
     if (in_dtype == ATTN_BF16)
         return run(0, s, "attn_fwd(bf16)", [&] { return attn::launch_fwd_bf16(a, out_dtype == ATTN_F32, s); });
     return run(0, s, "attn_fwd(fp32)", [&] { return attn::launch_fwd_f32(a, s); });
@@ -233,6 +235,37 @@ int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, i
                        hip_stream);
 }
 
+int attn_fwd_acc(const void* Q, const void* K, const void* V, const float* O_acc, const float* lse_acc, void* O,
+                 float* LSE, int B, int H, int N_q, int N_kv, int d, int causal, float scale, long long causal_offset,
+                 long long kv_head_stride, attn_dtype in_dtype, attn_dtype out_dtype, void* hip_stream) {
+    g_last_error.clear();
+    if (!O_acc || !lse_acc) return fail(ATTN_ERR_NULL_PTR, "O_acc and lse_acc must be non-NULL");
+    FwdCheck c;
+    int st = check_fwd(Q, K, V, O, LSE, B, H, N_q, N_kv, d, scale, kv_head_stride, in_dtype, out_dtype, &c);
+    if (st) return st;
+    const size_t acc_bytes = c.lse_bytes * (size_t)d;   // fp32 [B,H,N_q,d]
+    if ((((uintptr_t)O_acc | (uintptr_t)lse_acc) & 3) != 0 || (in_dtype == ATTN_BF16 && !aligned16(O_acc)))
+        return fail(ATTN_ERR_MISALIGNED, "O_acc must be 16-byte (bf16 inputs) or 4-byte aligned, lse_acc 4-byte");
+    const void* ins[3] = {Q, K, V};
+    const size_t in_n[3] = {c.q_bytes, c.kv_bytes, c.kv_bytes};
+    for (int i = 0; i < 3; ++i)
+        if (overlap(O_acc, acc_bytes, ins[i], in_n[i]) || overlap(lse_acc, c.lse_bytes, ins[i], in_n[i]))
+            return fail(ATTN_ERR_BAD_ALIAS, "O_acc or lse_acc overlaps an input (Q, K or V)");
+    // O may be exactly O_acc (fp32 output) and LSE exactly lse_acc; any other overlap is forbidden
+    if ((const void*)O == (const void*)O_acc) {
+        if (out_dtype != ATTN_F32) return fail(ATTN_ERR_BAD_ALIAS, "in-place accumulation needs an fp32 output");
+    } else if (overlap(O, c.o_bytes, O_acc, acc_bytes)) {
+        return fail(ATTN_ERR_BAD_ALIAS, "O partially overlaps O_acc");
+    }
+    if (LSE != lse_acc && overlap(LSE, c.lse_bytes, lse_acc, c.lse_bytes))
+        return fail(ATTN_ERR_BAD_ALIAS, "LSE partially overlaps lse_acc");
+    if (overlap(O, c.o_bytes, lse_acc, c.lse_bytes) || overlap(LSE, c.lse_bytes, O_acc, acc_bytes) ||
+        overlap(O_acc, acc_bytes, lse_acc, c.lse_bytes))
+        return fail(ATTN_ERR_BAD_ALIAS, "an output array overlaps the other partial array");
+    return launch_fwd(Q, K, V, O, LSE, B, H, N_q, N_kv, d, causal, scale, causal_offset, c.kv_stride, in_dtype,
+                      out_dtype, (hipStream_t)hip_stream, O_acc, lse_acc);
+}
+
 int attn_merge(const void* O_a, const float* lse_a, const void* O_b, const float* lse_b, void* O, float* lse,
                long long rows, int d, attn_dtype in_dtype, attn_dtype out_dtype, void* hip_stream) {
     g_last_error.clear();
@@ -268,7 +301,7 @@ size_t attn_fwd_chunked_workspace_bytes(int B, int H, int N_q, int d, int P) {
     if (B < 1 || H < 1 || N_q < 1 || d < 1 || P < 1) return 0;
     if (P == 1) return 0;
     const size_t rows = (size_t)B * H * N_q;
-    return 2 * align256(rows * d * sizeof(float)) + 2 * align256(rows * sizeof(float));
+    return align256(rows * d * sizeof(float)) + align256(rows * sizeof(float));
 }
 
 int attn_fwd_chunked(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q,
@@ -306,24 +339,23 @@ int attn_fwd_chunked(const void* Q, const void* K, const void* V, void* O, float
     const size_t rows = (size_t)B * H * N_q;
     char* ws = static_cast<char*>(workspace);
     float* o_acc = reinterpret_cast<float*>(ws);
-    float* o_p = reinterpret_cast<float*>(ws + align256(rows * d * sizeof(float)));
-    float* lse_acc = reinterpret_cast<float*>(ws + 2 * align256(rows * d * sizeof(float)));
-    float* lse_p = reinterpret_cast<float*>(ws + 2 * align256(rows * d * sizeof(float)) + align256(rows * sizeof(float)));
+    float* lse_acc = reinterpret_cast<float*>(ws + align256(rows * d * sizeof(float)));
     const size_t es = esize(dtype);
-    auto chunk = [&](int p, void* o, float* lse, attn_dtype out_t) {
+    // chunk p into (o, lse); every chunk after the first live one folds into the running partial in its
+    // own epilogue (in place in the workspace, or into O and LSE for the last one)
+    auto chunk = [&](int p, void* o, float* lse, attn_dtype out_t, const float* prev_o, const float* prev_lse) {
         const long long lo = (long long)p * N_kv / P, hi = (long long)(p + 1) * N_kv / P;
         const char* kp = static_cast<const char*>(K) + lo * d * es;
         const char* vp = static_cast<const char*>(V) + lo * d * es;
         return launch_fwd(Q, kp, vp, o, lse, B, H, N_q, (int)(hi - lo), d, causal, scale, offset - lo, c.kv_stride,
-                          dtype, out_t, s);
+                          dtype, out_t, s, prev_o, prev_lse);
     };
-    if (live.size() == 1) return chunk(live[0], O, LSE, dtype);
-    if ((st = chunk(live[0], o_acc, lse_acc, ATTN_F32))) return st;
+    if (live.size() == 1) return chunk(live[0], O, LSE, dtype, nullptr, nullptr);
+    if ((st = chunk(live[0], o_acc, lse_acc, ATTN_F32, nullptr, nullptr))) return st;
     for (size_t i = 1; i < live.size(); ++i) {
-        if ((st = chunk(live[i], o_p, lse_p, ATTN_F32))) return st;
         const bool last = i + 1 == live.size();
-        st = last ? launch_merge(o_acc, lse_acc, o_p, lse_p, O, LSE, (long long)rows, d, ATTN_F32, dtype, s)
-                  : launch_merge(o_acc, lse_acc, o_p, lse_p, o_acc, lse_acc, (long long)rows, d, ATTN_F32, ATTN_F32, s);
+        st = last ? chunk(live[i], O, LSE, dtype, o_acc, lse_acc)
+                  : chunk(live[i], o_acc, lse_acc, ATTN_F32, o_acc, lse_acc);
         if (st) return st;
     }
     return ATTN_OK;

@@ -133,6 +133,74 @@ __device__ __forceinline__ void lds_barrier() {
     __asm__ volatile("" ::: "memory");
 }
 
+// One query row's result from a bf16 kernel: O = acc / l and lse = m*|scale| + ln(l), or (0, -inf) when the
+// row saw no key; when the launch accumulates, folded into the running partial with the two-term merge
+// (M = max of the two lse, weights exp(lse - M) normalised to sum 1, lse = M + ln of their sum).  Lane h
+// of the row's half-wave pair holds head-dim elements 32*db + 8*g + 4*h + (0..3) of acc[db].
+// The previous partial's row (this lane's 4*NDB vectors) and lse, loaded ahead of the epilogue.
+template <int NDB>
+struct PrevRow {
+    f32x4 o[4 * NDB];
+    float lse;
+};
+
+template <int NDB>
+__device__ __forceinline__ void load_prev(const FwdArgs& a, int bh, int qi, int h, PrevRow<NDB>& pr) {
+    constexpr int D = 32 * NDB;
+    const float* op = a.o_prev + (size_t)bh * a.q_head_stride + (size_t)qi * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) pr.o[4 * db + g] = *reinterpret_cast<const f32x4*>(op + 32 * db + 8 * g + 4 * h);
+    pr.lse = a.lse_prev[(size_t)bh * a.n_q + qi];
+}
+
+template <int NDB, bool OUT_F32>
+__device__ __forceinline__ void store_row(const FwdArgs& a, int bh, int qi, int h, const f32x16 (&acc)[NDB],
+                                          float l_tot, float m, float scale_abs, const PrevRow<NDB>* pre = nullptr) {
+    constexpr int D = 32 * NDB;
+    const float lb = l_tot > 0.f ? m * scale_abs + logf(l_tot) : -INFINITY;
+    float cb = l_tot > 0.f ? 1.f / l_tot : 0.f;   // factor on this launch's accumulator
+    float ca = 0.f;                               // factor on the previous partial
+    float lse = lb;
+    const float* op = nullptr;
+    if (a.o_prev) {
+        const float la = pre ? pre->lse : a.lse_prev[(size_t)bh * a.n_q + qi];
+        const float big = fmaxf(la, lb);
+        if (big != -INFINITY) {
+            const float wa = expf(la - big), wb = expf(lb - big);
+            const float inv = 1.f / (wa + wb);
+            ca = wa * inv;
+            cb *= wb * inv;
+            lse = big + logf(wa + wb);
+        } else {
+            cb = 0.f;
+            lse = -INFINITY;
+        }
+        op = a.o_prev + (size_t)bh * a.q_head_stride + (size_t)qi * D;
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int c0 = 32 * db + 8 * g + 4 * h;
+            f32x4 o4 = {acc[db][4 * g] * cb, acc[db][4 * g + 1] * cb, acc[db][4 * g + 2] * cb, acc[db][4 * g + 3] * cb};
+            if (op) {
+                const f32x4 p4 = pre ? pre->o[4 * db + g] : *reinterpret_cast<const f32x4*>(op + c0);
+                o4 += ca * p4;
+            }
+            if (OUT_F32) {
+                float* oh = static_cast<float*>(a.o) + (size_t)bh * a.q_head_stride + (size_t)qi * D;
+                *reinterpret_cast<f32x4*>(oh + c0) = o4;
+            } else {
+                uint16_t* oh = static_cast<uint16_t*>(a.o) + (size_t)bh * a.q_head_stride + (size_t)qi * D;
+                const u32x2 o2 = {pack_bf16(o4[0], o4[1]), pack_bf16(o4[2], o4[3])};
+                *reinterpret_cast<u32x2*>(oh + c0) = o2;
+            }
+        }
+    if (h == 0) a.lse[(size_t)bh * a.n_q + qi] = lse;
+}
+
 // ---- Two-stage pipeline (used for d = 64): workgroups of four waves (128 query rows), two per CU.  K is
 // double-buffered and V triple-buffered.  Iteration t computes S(t) and the weights of tile t, and the P.V
 // product of tile t-1: the softmax of one tile shares a basic block with the P.V MFMAs of the previous one,
@@ -469,33 +537,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd
     for (int qb = 0; qb < QB; ++qb) {
         const int qi = qw0 + 32 * qb + col;
         const float l_tot = l[qb] + wave_xor32(l[qb]);
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        if (qi < a.n_q) {
-            if (OUT_F32) {
-                float* oh = static_cast<float*>(a.o) + (size_t)bh * a.q_head_stride + (size_t)qi * D;
-#pragma unroll
-                for (int db = 0; db < T::NDB; ++db)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const f32x16& ac = acc[qb][db];
-                        f32x4 o4 = {ac[4 * g] * inv, ac[4 * g + 1] * inv, ac[4 * g + 2] * inv, ac[4 * g + 3] * inv};
-                        *reinterpret_cast<f32x4*>(oh + 32 * db + 8 * g + 4 * h) = o4;
-                    }
-            } else {
-                uint16_t* oh = static_cast<uint16_t*>(a.o) + (size_t)bh * a.q_head_stride + (size_t)qi * D;
-#pragma unroll
-                for (int db = 0; db < T::NDB; ++db)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const f32x16& ac = acc[qb][db];
-                        u32x2 o2 = {pack_bf16(ac[4 * g] * inv, ac[4 * g + 1] * inv),
-                                    pack_bf16(ac[4 * g + 2] * inv, ac[4 * g + 3] * inv)};
-                        *reinterpret_cast<u32x2*>(oh + 32 * db + 8 * g + 4 * h) = o2;
-                    }
-            }
-            if (h == 0)
-                a.lse[(size_t)bh * a.n_q + qi] = l_tot > 0.f ? m[qb] * scale_abs + logf(l_tot) : -INFINITY;
-        }
+        if (qi < a.n_q) store_row<T::NDB, OUT_F32>(a, bh, qi, h, acc[qb], l_tot, m[qb], scale_abs);
     }
 }
 
@@ -836,6 +878,7 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
     // Steps 0 .. nt-1 (step t: softmax of tile t, P.V of t-1, S of t+1), then the P.V of the last tile.
     const int nt = wave_tiles;
     int t = 0;
+    PrevRow<T::NDB> prev;
     if (nt > 0) {
         s_all(s, kbuf_of(0));
         if (nt > 1) {
@@ -853,6 +896,8 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
         // tile visible (every wave waited for its loads of it), and it does not reload that V buffer
         retire(t);
         ++t;
+        // a running partial to fold into: its row is loaded now, to arrive during the last P.V
+        if (a.o_prev && qw0 + col < a.n_q) load_prev<T::NDB>(a, bh, qw0 + col, h, prev);
         step(no{}, yes{}, no{}, t, kbuf_of(t), kbuf_of(t), vbuf_of(nt - 1));
     }
     for (; t < ntiles; ++t) retire(t);   // the rest of the workgroup's barriers and loads
@@ -861,32 +906,7 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
     {
         const int qi = qw0 + col;
         const float l_tot = l + wave_xor32(l);
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        if (qi < a.n_q) {
-            if (OUT_F32) {
-                float* oh = static_cast<float*>(a.o) + (size_t)bh * a.q_head_stride + (size_t)qi * D;
-#pragma unroll
-                for (int db = 0; db < T::NDB; ++db)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const f32x16& ac = acc[db];
-                        f32x4 o4 = {ac[4 * g] * inv, ac[4 * g + 1] * inv, ac[4 * g + 2] * inv, ac[4 * g + 3] * inv};
-                        *reinterpret_cast<f32x4*>(oh + 32 * db + 8 * g + 4 * h) = o4;
-                    }
-            } else {
-                uint16_t* oh = static_cast<uint16_t*>(a.o) + (size_t)bh * a.q_head_stride + (size_t)qi * D;
-#pragma unroll
-                for (int db = 0; db < T::NDB; ++db)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const f32x16& ac = acc[db];
-                        u32x2 o2 = {pack_bf16(ac[4 * g] * inv, ac[4 * g + 1] * inv),
-                                    pack_bf16(ac[4 * g + 2] * inv, ac[4 * g + 3] * inv)};
-                        *reinterpret_cast<u32x2*>(oh + 32 * db + 8 * g + 4 * h) = o2;
-                    }
-            }
-            if (h == 0) a.lse[(size_t)bh * a.n_q + qi] = l_tot > 0.f ? m * scale_abs + logf(l_tot) : -INFINITY;
-        }
+        if (qi < a.n_q) store_row<T::NDB, OUT_F32>(a, bh, qi, h, acc, l_tot, m, scale_abs, nt > 0 ? &prev : nullptr);
     }
 }
 

@@ -109,16 +109,35 @@ __global__ __launch_bounds__(F_THREADS) void fwd_f32_kernel(FwdArgs a, int num_q
     }
 
     if (!q_ok) return;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    // O = acc / l and lse = m + ln(l) (or (0, -inf)); when the launch accumulates, folded into the running
+    // partial with the two-term merge of the (O, lse) merge kernel
+    const float lb = l > 0.f ? (float)(m + (double)logf(l)) : -INFINITY;
+    float cb = l > 0.f ? 1.f / l : 0.f, ca = 0.f, lse = lb;
+    const float* op = nullptr;
+    if (a.o_prev) {
+        const float la = a.lse_prev[(size_t)bh * a.n_q + qi];
+        const float big = fmaxf(la, lb);
+        if (big != -INFINITY) {
+            const float wa = expf(la - big), wb = expf(lb - big);
+            const float inv = 1.f / (wa + wb);
+            ca = wa * inv;
+            cb *= wb * inv;
+            lse = big + logf(wa + wb);
+        } else {
+            cb = 0.f;
+            lse = -INFINITY;
+        }
+        op = a.o_prev + (size_t)bh * a.q_head_stride + (size_t)qi * d;
+    }
     float* oh = static_cast<float*>(a.o) + (size_t)bh * a.q_head_stride + (size_t)qi * d;
 #pragma unroll
     for (int i = 0; i < NCH; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int cc = 16 * i + 4 * r + e;
-            if (cc < d) oh[cc] = acc[i][e] * inv;
+            if (cc < d) oh[cc] = acc[i][e] * cb + (op ? ca * op[cc] : 0.f);
         }
-    if (r == 0) a.lse[(size_t)bh * a.n_q + qi] = l > 0.f ? (float)(m + (double)logf(l)) : -INFINITY;
+    if (r == 0) a.lse[(size_t)bh * a.n_q + qi] = lse;
 }
 
 template <int DMAX>

@@ -18,6 +18,11 @@ struct FwdArgs {
     int causal;
     int offset;             // key j visible to query i iff j <= i + offset (clamped to [-n_q-1, n_kv])
     float scale;            // signed logit scale
+    // Running partial to fold this launch's result into (both NULL: plain store).  fp32, laid out like O
+    // (o_prev) and LSE (lse_prev); o_prev may equal o (fp32 output) and lse_prev may equal lse, since every
+    // row is read and written by the lanes that own it.
+    const float* o_prev;
+    const float* lse_prev;
 };
 
 struct MergeArgs {

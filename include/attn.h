@@ -87,6 +87,23 @@ int attn_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE
                 attn_dtype in_dtype, attn_dtype out_dtype, void* hip_stream);
 
 /*
+ * attn_fwd_acc - attn_fwd_ex folded into a running partial result in the same launch:
+ *     (O, LSE) = merge((O_acc, lse_acc), attention of Q against this key range)
+ * with the merge of attn_merge.  The kernel's epilogue reads the partial row by row and writes the merged
+ * row, so no separate merge pass and no partial of this range ever reaches memory.
+ *   O_acc [B,H,N_q,d] and lse_acc [B,H,N_q] fp32 hold the result over the keys seen so far (a row with
+ *   lse_acc = -inf is empty); the other arguments are those of attn_fwd_ex.  O is fp32 or the input dtype.
+ *   In place is allowed: O == O_acc (with an fp32 O) and LSE == lse_acc; any other overlap between O, LSE,
+ *   O_acc, lse_acc, Q, K and V is ATTN_ERR_BAD_ALIAS.  O_acc must be 16-byte aligned for bf16 inputs.
+ * Source: "ATTENTION2D" explainer, sections 2 and 3 (partial statistics combined as they arrive), applied
+ * at the end of each key range of "Ring Attention with Blockwise Parallel Transformers", section 3.
+ */
+int attn_fwd_acc(const void* Q, const void* K, const void* V, const float* O_acc, const float* lse_acc,
+                 void* O, float* LSE, int B, int H, int N_q, int N_kv, int d, int causal, float scale,
+                 long long causal_offset, long long kv_head_stride,
+                 attn_dtype in_dtype, attn_dtype out_dtype, void* hip_stream);
+
+/*
  * attn_merge - combine two partial results over disjoint key sets, row by row:
  *     M = max(lse_a, lse_b);  w_x = exp(lse_x - M);  O = (w_a O_a + w_b O_b) / (w_a + w_b);
  *     lse = M + ln(w_a + w_b);  rows with M = -inf give (0, -inf).
@@ -101,18 +118,19 @@ int attn_merge(const void* O_a, const float* lse_a, const void* O_b, const float
                attn_dtype in_dtype, attn_dtype out_dtype, void* hip_stream);
 
 /*
- * attn_fwd_chunked_workspace_bytes - device workspace attn_fwd_chunked needs: two fp32 partial outputs
- * [B,H,N_q,d] and two fp32 lse rows [B,H,N_q], each 256-byte aligned; 0 when P == 1.
+ * attn_fwd_chunked_workspace_bytes - device workspace attn_fwd_chunked needs: one fp32 partial output
+ * [B,H,N_q,d] and one fp32 lse row [B,H,N_q], each 256-byte aligned; 0 when P == 1.
  * Returns 0 as well for invalid arguments (attn_fwd_chunked reports those).
  */
 size_t attn_fwd_chunked_workspace_bytes(int B, int H, int N_q, int d, int P);
 
 /*
  * attn_fwd_chunked - the keys are cut into P contiguous chunks, chunk p covering
- * [floor(p*N_kv/P), floor((p+1)*N_kv/P)); each chunk is attended with attn_fwd_ex into fp32 partials and
- * folded left to right with attn_merge; the last merge writes O in `dtype` and LSE.  Chunks that are
- * empty or entirely in the causal future are skipped (they are the merge identity).  Result: equal to
- * attn_fwd up to rounding.  P >= 1 (P > N_kv is allowed).  Everything is enqueued on one stream.
+ * [floor(p*N_kv/P), floor((p+1)*N_kv/P)), and folded left to right: the first chunk is attended with
+ * attn_fwd_ex into an fp32 partial in the workspace, every later one with attn_fwd_acc (in place in the
+ * workspace, the last one writing O in `dtype` and LSE).  Chunks that are empty or entirely in the causal
+ * future are skipped (they are the merge identity).  Result: equal to attn_fwd up to rounding.  P >= 1
+ * (P > N_kv is allowed).  Everything is enqueued on one stream.
  * Source: "Ring Attention with Blockwise Parallel Transformers" explainer, section 3 (key/value blocks
  * visited one after another), and "ATTENTION2D" explainer, section 3 (staged combination).
  */

@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = A.lib()
     names = declared_functions()
-    assert {"attn_fwd", "attn_fwd_ex", "attn_merge", "attn_fwd_chunked", "attn_fwd_chunked_workspace_bytes",
+    assert {"attn_fwd", "attn_fwd_ex", "attn_fwd_acc", "attn_merge", "attn_fwd_chunked", "attn_fwd_chunked_workspace_bytes",
             "attn_strerror", "attn_last_error", "attn_timing_enable", "attn_timing_read"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in attn.h but not exported"
@@ -53,6 +53,11 @@ def fwd_ex(*, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=2, N_q=8, N_kv=8,
 
 def merge(*, oa=P[0], la=P[1], ob=P[2], lb=P[3], o=P[4], lse=P[5], rows=16, d=64, din=A.ATTN_F32, dout=A.ATTN_F32):
     return A.lib().attn_merge(oa, la, ob, lb, o, lse, rows, d, din, dout, None)
+
+
+def fwd_acc(*, q=P[0], k=P[1], v=P[2], oa=P[5], la=P[6], o=P[3], lse=P[4], B=1, H=2, N_q=8, N_kv=8, d=64,
+            din=A.ATTN_BF16, dout=A.ATTN_BF16):
+    return A.lib().attn_fwd_acc(q, k, v, oa, la, o, lse, B, H, N_q, N_kv, d, 0, 0.125, 0, 0, din, dout, None)
 
 
 def chunked(*, o=P[3], lse=P[4], P_=4, ws=P[6], ws_n=1 << 40, d=64, dtype=A.ATTN_BF16, N_q=8, N_kv=8):
@@ -132,8 +137,8 @@ def test_workspace_formula():
     assert f(1, 2, 8, 64, 1) == 0
     rows = 1 * 32 * 16384
     a256 = lambda x: (x + 255) // 256 * 256
-    assert f(1, 32, 16384, 128, 8) == 2 * a256(rows * 128 * 4) + 2 * a256(rows * 4)
-    assert f(1, 1, 3, 5, 2) == 2 * 256 + 2 * 256
+    assert f(1, 32, 16384, 128, 8) == a256(rows * 128 * 4) + a256(rows * 4)
+    assert f(1, 1, 3, 5, 2) == 256 + 256
     assert f(0, 1, 1, 64, 2) == 0 and f(1, 1, 1, 64, 0) == 0
 
 
@@ -153,3 +158,18 @@ def test_timing_read_without_launches():
 def test_python_errors_name_the_status():
     err = A.AttnError(3, "attn_fwd", "x")
     assert "ATTN_ERR_UNSUPPORTED_D" in str(err) and err.status == 3
+
+
+def test_fwd_acc_validation():
+    assert fwd_acc(oa=None) == 1 and "O_acc" in last_error()
+    assert fwd_acc(la=None) == 1
+    assert fwd_acc(d=100) == 3
+    assert fwd_acc(oa=ctypes.c_void_p(P[5].value + 8)) == 9            # bf16 inputs: O_acc 16-byte aligned
+    assert fwd_acc(la=ctypes.c_void_p(P[6].value + 2)) == 9
+    assert fwd_acc(oa=P[0]) == 7 and "overlaps an input" in last_error()   # O_acc over Q
+    assert fwd_acc(la=P[2]) == 7                                        # lse_acc over V
+    assert fwd_acc(o=P[5]) == 7 and "fp32 output" in last_error()       # in place needs an fp32 O
+    assert fwd_acc(o=ctypes.c_void_p(P[5].value + 64), dout=A.ATTN_F32) == 7   # partial overlap of O and O_acc
+    assert fwd_acc(lse=ctypes.c_void_p(P[6].value + 4)) == 7            # partial overlap of LSE and lse_acc
+    assert fwd_acc(la=ctypes.c_void_p(P[5].value + 256)) == 7           # lse_acc inside O_acc
+    assert fwd_acc(din=A.ATTN_F32, dout=A.ATTN_BF16) == 4

@@ -199,6 +199,47 @@ def test_key_range_and_offset_partials():
     assert_parity(err, "bf16", "partial a")
 
 
+# ------------------------------------------------------------------------- fused fold of a key range (acc)
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 37)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_acc_vs_oracle(dt, d, causal):
+    """attn_fwd_acc folds key ranges into a running fp32 partial in the kernel epilogue: three ranges
+    (the middle one folded in place, the last one written in the input dtype) equal the whole; the causal
+    case has query rows that see nothing in the later ranges and rows that see nothing in the first."""
+    w = W.Workload("acc", 1, 2, 300, 700, d, dt, causal, 1, seed=2300 + d + 7 * causal)
+    st, (q, k, v) = make(w)
+    o_ref, l_ref = oracle_full(st, w)
+    off = w.N_kv - w.N_q if causal else 0
+    a, b = 250, 520
+    oa, la = A.fwd_ex(q, k, v, causal, w.scale, causal_offset=off, key_range=(0, a), out_dtype=torch.float32)
+    res = A.fwd_acc(q, k, v, oa, la, causal, w.scale, causal_offset=off - a, key_range=(a, b),
+                    out_dtype=torch.float32, out=oa, lse=la)
+    assert res[0].data_ptr() == oa.data_ptr()
+    o, lse = A.fwd_acc(q, k, v, oa, la, causal, w.scale, causal_offset=off - b, key_range=(b, w.N_kv))
+    torch.cuda.synchronize()
+    err = errors(out_to_f64(o), out_to_f64(lse), o_ref, l_ref)
+    print(w, err, flush=True)
+    assert_parity(err, dt, f"three ranges folded, {dt} d{d}")
+    # the same fold against the separate merge kernel: equal up to rounding
+    ob, lb = A.fwd_ex(q, k, v, causal, w.scale, causal_offset=off - b, key_range=(b, w.N_kv),
+                      out_dtype=torch.float32)
+    om, lm = A.merge(oa, la, ob, lb, out_dtype=q.dtype)
+    torch.cuda.synchronize()
+    assert_parity(errors(out_to_f64(o), out_to_f64(lse), out_to_f64(om), out_to_f64(lm)), dt, "fold vs merge")
+
+
+def test_fwd_acc_empty_partial_is_identity():
+    """A partial of all-empty rows (lse = -inf, O = 0) folded with a range gives that range's result."""
+    w = W.Workload("acc0", 1, 2, 200, 300, 128, "bf16", False, 1, seed=2400)
+    st, (q, k, v) = make(w)
+    o_ref, l_ref = oracle_full(st, w)
+    oa = torch.zeros((1, 2, 200, 128), dtype=torch.float32, device="cuda")
+    la = torch.full((1, 2, 200), -math.inf, dtype=torch.float32, device="cuda")
+    o, lse = A.fwd_acc(q, k, v, oa, la, False, w.scale)
+    torch.cuda.synchronize()
+    assert_parity(errors(out_to_f64(o), out_to_f64(lse), o_ref, l_ref), "bf16", "identity partial")
+
+
 # ------------------------------------------------------------------------------------------------- merge
 @pytest.mark.parametrize("din,dout,d", [("f32", "f32", 128), ("f32", "bf16", 128), ("bf16", "bf16", 64),
                                         ("f32", "f32", 37), ("bf16", "f32", 5)])
