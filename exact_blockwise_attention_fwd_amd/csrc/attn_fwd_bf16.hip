@@ -64,6 +64,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float REF_BOUND = 18446744073709551616.0f;   // 2^64: largest weight sum taken against a stale reference
@@ -137,27 +138,9 @@ __device__ __forceinline__ void lds_barrier() {
 // row saw no key; when the launch accumulates, folded into the running partial with the two-term merge
 // (M = max of the two lse, weights exp(lse - M) normalised to sum 1, lse = M + ln of their sum).  Lane h
 // of the row's half-wave pair holds head-dim elements 32*db + 8*g + 4*h + (0..3) of acc[db].
-// The previous partial's row (this lane's 4*NDB vectors) and lse, loaded ahead of the epilogue.
-template <int NDB>
-struct PrevRow {
-    f32x4 o[4 * NDB];
-    float lse;
-};
-
-template <int NDB>
-__device__ __forceinline__ void load_prev(const FwdArgs& a, int bh, int qi, int h, PrevRow<NDB>& pr) {
-    constexpr int D = 32 * NDB;
-    const float* op = a.o_prev + (size_t)bh * a.q_head_stride + (size_t)qi * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) pr.o[4 * db + g] = *reinterpret_cast<const f32x4*>(op + 32 * db + 8 * g + 4 * h);
-    pr.lse = a.lse_prev[(size_t)bh * a.n_q + qi];
-}
-
 template <int NDB, bool OUT_F32>
 __device__ __forceinline__ void store_row(const FwdArgs& a, int bh, int qi, int h, const f32x16 (&acc)[NDB],
-                                          float l_tot, float m, float scale_abs, const PrevRow<NDB>* pre = nullptr) {
+                                          float l_tot, float m, float scale_abs) {
     constexpr int D = 32 * NDB;
     const float lb = l_tot > 0.f ? m * scale_abs + logf(l_tot) : -INFINITY;
     float cb = l_tot > 0.f ? 1.f / l_tot : 0.f;   // factor on this launch's accumulator
@@ -165,7 +148,7 @@ __device__ __forceinline__ void store_row(const FwdArgs& a, int bh, int qi, int 
     float lse = lb;
     const float* op = nullptr;
     if (a.o_prev) {
-        const float la = pre ? pre->lse : a.lse_prev[(size_t)bh * a.n_q + qi];
+        const float la = a.lse_prev[(size_t)bh * a.n_q + qi];
         const float big = fmaxf(la, lb);
         if (big != -INFINITY) {
             const float wa = expf(la - big), wb = expf(lb - big);
@@ -186,8 +169,7 @@ __device__ __forceinline__ void store_row(const FwdArgs& a, int bh, int qi, int 
             const int c0 = 32 * db + 8 * g + 4 * h;
             f32x4 o4 = {acc[db][4 * g] * cb, acc[db][4 * g + 1] * cb, acc[db][4 * g + 2] * cb, acc[db][4 * g + 3] * cb};
             if (op) {
-                const f32x4 p4 = pre ? pre->o[4 * db + g] : *reinterpret_cast<const f32x4*>(op + c0);
-                o4 += ca * p4;
+                o4 += ca * *reinterpret_cast<const f32x4*>(op + c0);
             }
             if (OUT_F32) {
                 float* oh = static_cast<float*>(a.o) + (size_t)bh * a.q_head_stride + (size_t)qi * D;
@@ -656,8 +638,18 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
         for (int k = 0; k < T::SEGS_PER_WAVE; ++k)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (wave + T::NW * k) * 1024), 16, v_voff + WS * k, 0, 0, 0);
     };
-    auto kbuf_of = [&](int j) __attribute__((always_inline)) { return (const lds_char*)(lds + (j % T::NK) * T::TILE); };
-    auto vbuf_of = [&](int j) __attribute__((always_inline)) { return (const lds_char*)(lds + (T::NK + (j % T::NV)) * T::TILE); };
+    // Buffer bases pass through an empty statement as scalars, so that the compiler cannot split a constant
+    // out of them into every read's address (it would be negative, which the offset field cannot hold).
+    auto kbuf_of = [&](int j) __attribute__((always_inline)) {
+        int o = (j % T::NK) * T::TILE;
+        __asm__ volatile("" : "+s"(o));
+        return (const lds_char*)(lds + o);
+    };
+    auto vbuf_of = [&](int j) __attribute__((always_inline)) {
+        int o = (T::NK + (j % T::NV)) * T::TILE;
+        __asm__ volatile("" : "+s"(o));
+        return (const lds_char*)(lds + o);
+    };
 
     // ---- Q^T fragments (B operand), held for the whole key loop
     const float scale_abs = fabsf(a.scale);
@@ -750,6 +742,12 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
     auto step = [&](auto do_soft, auto do_pv, auto do_s, int t, const lds_char* __restrict__ kn,
                     const lds_char* __restrict__ kc, const lds_char* __restrict__ vp) __attribute__((always_inline)) {
         constexpr bool SOFT = decltype(do_soft)::value, PV = decltype(do_pv)::value, S = decltype(do_s)::value;
+        // The per-lane LDS offsets pass through an empty statement, so that "buffer + offset" is formed once
+        // per offset and step and the (kb, ks) constants land in the reads' offset fields.
+#pragma unroll
+        for (int ks = 0; ks < T::NKS; ++ks) __asm__ volatile("" : "+v"(k_roff[ks]));
+#pragma unroll
+        for (int db = 0; db < T::NDB; ++db) __asm__ volatile("" : "+v"(v_roff[db]));
         // a reference moved by the previous softmax: rescale the output before P.V(t-1) adds to it
         if (moved) {
 #pragma unroll
@@ -878,7 +876,25 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
     // Steps 0 .. nt-1 (step t: softmax of tile t, P.V of t-1, S of t+1), then the P.V of the last tile.
     const int nt = wave_tiles;
     int t = 0;
-    PrevRow<T::NDB> prev;
+    // The wave's 32 rows of the running partial (when there is one) and of the output are addressed through
+    // buffer resources bounded at the last query row: loads past it return zeros and stores are dropped.
+    const int rows_left = __builtin_amdgcn_readfirstlane(max(0, min(32, a.n_q - qw0)));   // uniform, kept scalar
+    // The running partial, in the order the epilogue writes: with fp32 output lane l holds floats
+    // 4*(l%32)..+3 of row 2k + l/32 in prev[k]; with bf16 output floats 8*(l%16) + 4*(k%2)..+3 of row
+    // 4*(k/2) + l/16.
+    f32x4 prev[16];
+    float lse_pv = -INFINITY;   // lse of the partial for row qw0 + col
+    auto fetch_prev = [&]() __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.o_prev + (size_t)bh * a.q_head_stride + (size_t)qw0 * D), (short)0, rows_left * D * 4, BUF_RSRC_WORD3);
+        const int voff = OUT_F32 ? (lane >> 5) * D * 4 + 16 * (lane & 31) : (lane >> 4) * D * 4 + 32 * (lane & 15);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int koff = OUT_F32 ? 2 * k * D * 4 : 4 * (k >> 1) * D * 4 + 16 * (k & 1);
+            prev[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, koff, 0));
+        }
+        if (col < rows_left) lse_pv = a.lse_prev[(size_t)bh * a.n_q + qw0 + col];
+    };
     if (nt > 0) {
         s_all(s, kbuf_of(0));
         if (nt > 1) {
@@ -896,17 +912,106 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
         // tile visible (every wave waited for its loads of it), and it does not reload that V buffer
         retire(t);
         ++t;
-        // a running partial to fold into: its row is loaded now, to arrive during the last P.V
-        if (a.o_prev && qw0 + col < a.n_q) load_prev<T::NDB>(a, bh, qw0 + col, h, prev);
+        // the running partial is loaded now, to arrive during the last P.V
+        if (a.o_prev) fetch_prev();
         step(no{}, yes{}, no{}, t, kbuf_of(t), kbuf_of(t), vbuf_of(nt - 1));
+    } else if (a.o_prev) {
+        fetch_prev();
     }
     for (; t < ntiles; ++t) retire(t);   // the rest of the workgroup's barriers and loads
 
-    // ---- epilogue: one division by the final denominator; lse = scaled reference + ln(l)
+    // ---- epilogue: one division by the final denominator, lse = scaled reference + ln(l), and the fold
+    // into the running partial (two-term merge: M = max of the two lse, weights exp(lse - M) normalised to
+    // sum 1, lse = M + ln of their sum).  Lane (col, h) holds head-dim elements 32*db + 8*g + 4*h + (0..3)
+    // of its row; the scaled rows go through LDS so that loads and stores cover whole rows.
     {
         const int qi = qw0 + col;
         const float l_tot = l + wave_xor32(l);
-        if (qi < a.n_q) store_row<T::NDB, OUT_F32>(a, bh, qi, h, acc, l_tot, m, scale_abs, nt > 0 ? &prev : nullptr);
+        const float lb = l_tot > 0.f ? m * scale_abs + logf(l_tot) : -INFINITY;
+        float cb = l_tot > 0.f ? 1.f / l_tot : 0.f;   // factor on this launch's accumulator
+        float ca = 0.f;                               // factor on the running partial
+        float lse = lb;
+        if (a.o_prev) {
+            const float big = fmaxf(lse_pv, lb);
+            if (big != -INFINITY) {
+                const float wa = expf(lse_pv - big), wb = expf(lb - big);
+                const float inv = 1.f / (wa + wb);
+                ca = wa * inv;
+                cb *= wb * inv;
+                lse = big + logf(wa + wb);
+            } else {
+                cb = 0.f;
+                lse = -INFINITY;
+            }
+        }
+        if (h == 0 && col < rows_left) a.lse[(size_t)bh * a.n_q + qi] = lse;
+        // A free 16 KiB LDS buffer per wave: after the last barrier only the V buffer of the last tile may
+        // still be read (by waves finishing their last P.V); nothing else is read or loaded any more.
+        const int busy = ntiles > 0 ? T::NK + (ntiles - 1) % T::NV : T::NK + T::NV;
+        const int slot = wave < busy ? wave : wave + 1;
+        lds_char* const st = lds + slot * T::TILE;
+        // row r, 16-byte piece q at piece q ^ r of the row (conflict-free writes and reads)
+#pragma unroll
+        for (int db = 0; db < T::NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int q = 8 * db + 2 * g + h;
+                const f32x4 o4 = {acc[db][4 * g] * cb, acc[db][4 * g + 1] * cb, acc[db][4 * g + 2] * cb,
+                                  acc[db][4 * g + 3] * cb};
+                *(lds_f32x4*)(st + col * 512 + 16 * (q ^ col)) = o4;
+            }
+        __asm__ volatile("" ::: "memory");   // the reads below see this wave's writes (LDS keeps a wave's order)
+        const int ca_bits = __builtin_bit_cast(int, ca);
+        const size_t obase = (size_t)bh * a.q_head_stride + (size_t)qw0 * D;
+        if constexpr (OUT_F32) {
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(static_cast<float*>(a.o) + obase), (short)0, rows_left * D * 4, BUF_RSRC_WORD3);
+            const int q = lane & 31;
+            f32x4 o4[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const int r = 2 * k + (lane >> 5);
+                o4[k] = *(const lds_f32x4*)(st + r * 512 + 16 * (q ^ r));
+            }
+            if (a.o_prev) {
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    const int r = 2 * k + (lane >> 5);
+                    o4[k] += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * r, ca_bits)) * prev[k];
+                }
+            }
+            const int voff = (lane >> 5) * D * 4 + 16 * q;
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o4[k]), rs, voff, 2 * k * D * 4, 0);
+        } else {
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(static_cast<uint16_t*>(a.o) + obase), (short)0, rows_left * D * 2, BUF_RSRC_WORD3);
+            const int q = lane & 15;
+            f32x4 lo[8], hi[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int r = 4 * k + (lane >> 4);
+                lo[k] = *(const lds_f32x4*)(st + r * 512 + 16 * ((2 * q) ^ r));
+                hi[k] = *(const lds_f32x4*)(st + r * 512 + 16 * ((2 * q + 1) ^ r));
+            }
+            if (a.o_prev) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int r = 4 * k + (lane >> 4);
+                    const float car = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * r, ca_bits));
+                    lo[k] += car * prev[2 * k];
+                    hi[k] += car * prev[2 * k + 1];
+                }
+            }
+            const int voff = (lane >> 4) * D * 2 + 16 * q;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const u32x4 o4 = {pack_bf16(lo[k][0], lo[k][1]), pack_bf16(lo[k][2], lo[k][3]),
+                                  pack_bf16(hi[k][0], hi[k][1]), pack_bf16(hi[k][2], hi[k][3])};
+                __builtin_amdgcn_raw_buffer_store_b128(o4, rs, voff, 4 * k * D * 2, 0);
+            }
+        }
     }
 }
 
