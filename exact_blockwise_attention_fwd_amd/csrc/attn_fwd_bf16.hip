@@ -254,8 +254,8 @@ __global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd
 #pragma unroll
         for (int k = 0; k < T::SEGS_PER_WAVE; ++k) {
             const int seg = wave + T::NW * k;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kbuf + seg * 1024), 16, k_voff + 4096 * k, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vbuf + seg * 1024), 16, v_voff + 4096 * k, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kbuf + seg * 1024), 16, k_voff, 4096 * k, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vbuf + seg * 1024), 16, v_voff, 4096 * k, 0, 0);
         }
     };
 
@@ -626,7 +626,7 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
             __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)kh + base), (short)0, (int)(kv_bytes - base), BUF_RSRC_WORD3);
 #pragma unroll
         for (int k = 0; k < T::SEGS_PER_WAVE; ++k)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (wave + T::NW * k) * 1024), 16, k_voff + WS * k, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (wave + T::NW * k) * 1024), 16, k_voff, WS * k, 0, 0);
     };
     auto load_v = [&](int j) __attribute__((always_inline)) {   // V_j into V buffer j % NV
         if (j >= ntiles) return;
@@ -636,7 +636,7 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
             __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)vh + base), (short)0, (int)(kv_bytes - base), BUF_RSRC_WORD3);
 #pragma unroll
         for (int k = 0; k < T::SEGS_PER_WAVE; ++k)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (wave + T::NW * k) * 1024), 16, v_voff + WS * k, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (wave + T::NW * k) * 1024), 16, v_voff, WS * k, 0, 0);
     };
     // Buffer bases pass through an empty statement as scalars, so that the compiler cannot split a constant
     // out of them into every read's address (it would be negative, which the offset field cannot hold).

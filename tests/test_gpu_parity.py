@@ -164,9 +164,10 @@ def test_unusual_scales(scale, dt):
     assert_parity(errors(out_to_f64(o), out_to_f64(lse), o_ref, l_ref), dt, f"scale={scale}")
 
 
-def test_peaky_sorted_keys_rescale_every_tile():
+@pytest.mark.parametrize("d", [64, 128])
+def test_peaky_sorted_keys_rescale_every_tile(d):
     """Keys sorted by ascending logit for query 0: its running max rises on every key tile."""
-    w = W.Workload("sorted", 1, 1, 256, 2048, 128, "bf16", False, 1, seed=2100, q_std=4.0)
+    w = W.Workload("sorted", 1, 1, 256, 2048, d, "bf16", False, 1, seed=2100, q_std=4.0)
     st, _ = make(w)
     q64 = storage_to_f64(st[0][0, 0])
     order = np.argsort(storage_to_f64(st[1][0, 0]) @ q64[0])
