@@ -570,6 +570,7 @@ struct P3 {
     static constexpr int LDS = (NK + NV) * TILE;
     static constexpr int WSTRIDE = NW * RPS * ROW;   // bytes between the load segments of one wave
     static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
+    static_assert(NK + NV >= NW + 1, "the epilogue stages every wave's rows in its own free K/V buffer");
 };
 
 template <int NW, bool CAUSAL, bool OUT_F32>
@@ -689,6 +690,8 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
     bool moved = false;
     f32x16 s[T::NKB];           // scores of the tile whose softmax is next
     u32x4 p[T::NKB][2];         // bf16 weights of the tile whose P.V is next
+    float mcr = 0.f;            // m*c, or 0 while the row has no reference
+    float bnd = -1.f;           // bound on a tile's weight sum: 2^64, or -1 (forcing the redo) while there is no reference
 
     auto s_all = [&](f32x16 (&sc)[T::NKB], const lds_char* kbuf) __attribute__((always_inline)) {
 #pragma unroll
@@ -757,9 +760,12 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
         if constexpr (SOFT) {
             if (t >= full_tiles) mask_tile(t, s);   // diagonal and ragged tiles
         }
-        const bool none = m == -INFINITY;
-        const float mc = none ? 0.f : m * c;
+        const float mc = mcr;
         float e[2 * 16];
+        u32x4 kv[16];
+        auto kread = [&](int i) __attribute__((always_inline)) {
+            kv[i] = *(const lds_u32x4*)(kn + k_roff[i >> 1] + 32 * (i & 1) * T::ROW);
+        };
         // ---- part 1: P.V(t-1) (two transpose reads per MFMA, two MFMAs ahead) with the exps of tile t
         {
             i16x4 vl[16], vhh[16];
@@ -787,17 +793,16 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
                     e[2 * i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i >> 3][(2 * i) & 15], c, -mc));
                     e[2 * i + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i >> 3][(2 * i + 1) & 15], c, -mc));
                 }
+                if constexpr (S && PV) {
+                    if (i >= 14) kread(i - 14);   // the first K operands of part 2, under the last P.V MFMAs
+                }
                 if constexpr (PV) __builtin_amdgcn_sched_barrier(0);
             }
         }
         // ---- part 2: S(t+1) (one K read per MFMA, two MFMAs ahead) with the sums and packs of tile t
-        float r[16];
+        float rs = 0.f;   // the tile's weight sum, accumulated pair by pair under the S MFMAs
         {
-            u32x4 kv[16];
-            auto kread = [&](int i) __attribute__((always_inline)) {
-                kv[i] = *(const lds_u32x4*)(kn + k_roff[i >> 1] + 32 * (i & 1) * T::ROW);
-            };
-            if constexpr (S) {
+            if constexpr (S && !PV) {
                 kread(0);
                 kread(1);
             }
@@ -810,7 +815,8 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
                     s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv[i]), qf[ks], ks == 0 ? f32x16{} : s[kb], 0, 0, 0);
                 }
                 if constexpr (SOFT) {
-                    r[i] = e[2 * i] + e[2 * i + 1];
+                    const float pair = e[2 * i] + e[2 * i + 1];
+                    rs = i == 0 ? pair : rs + pair;
                     p[i >> 3][(i >> 2) & 1][i & 3] = pack_bf16(e[2 * i], e[2 * i + 1]);
                     __asm__ volatile("" ::"v"(p[i >> 3][(i >> 2) & 1][i & 3]));   // keep the pack in this slot
                 }
@@ -818,13 +824,8 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
             }
         }
         if constexpr (SOFT) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) r[j] = r[2 * j] + r[2 * j + 1];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) r[j] = r[2 * j] + r[2 * j + 1];
-            float rs = (r[0] + r[1]) + (r[2] + r[3]);
             float alpha = 1.f;
-            if (__any(none || !(rs <= REF_BOUND))) {
+            if (__any(!(rs <= bnd))) {
                 // rare: no reference yet, or a weight sum above 2^64.  Tile t's scores were replaced by
                 // S(t+1) (when there was one): recompute them from K_t, mask, and redo the tile against its max.
                 f32x16 sc[T::NKB];
@@ -848,7 +849,9 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
                     moved = true;
                 }
                 m = m_new;
-                rs = weights(sc, m_new == -INFINITY ? 0.f : m_new * c);
+                mcr = m_new == -INFINITY ? 0.f : m_new * c;
+                bnd = m_new == -INFINITY ? -1.f : REF_BOUND;
+                rs = weights(sc, mcr);
             }
             l = __builtin_fmaf(l, alpha, rs);
         }
