@@ -70,13 +70,29 @@ int run(int kind, hipStream_t s, const char* what, F&& launch) {
             timed = e0 && e1;
         }
     }
-    if (timed && hipEventRecord(e0, s) != hipSuccess) return fail(ATTN_ERR_HIP, "%s: hipEventRecord failed", what);
+    auto give_back = [&] {   // events of a launch that will not be timed go back to the pool
+        std::lock_guard<std::mutex> g(g_timing_mu);
+        if (e0) g_event_pool.push_back(e0);
+        if (e1) g_event_pool.push_back(e1);
+    };
+    if (timed && hipEventRecord(e0, s) != hipSuccess) {
+        give_back();
+        return fail(ATTN_ERR_HIP, "%s: hipEventRecord failed", what);
+    }
     hipError_t err = launch();
-    if (err != hipSuccess) return fail(ATTN_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(err));
+    if (err != hipSuccess) {
+        give_back();
+        return fail(ATTN_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(err));
+    }
     if (timed) {
-        if (hipEventRecord(e1, s) != hipSuccess) return fail(ATTN_ERR_HIP, "%s: hipEventRecord failed", what);
+        if (hipEventRecord(e1, s) != hipSuccess) {
+            give_back();
+            return fail(ATTN_ERR_HIP, "%s: hipEventRecord failed", what);
+        }
         std::lock_guard<std::mutex> g(g_timing_mu);
         g_timed.push_back({kind, e0, e1});
+    } else if (e0 || e1) {
+        give_back();
     }
     if (debug_sync()) {
         err = hipStreamSynchronize(s);

@@ -523,6 +523,21 @@ __global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd
     }
 }
 
+// LDS above the default limit needs an explicit opt-in, once per kernel and device.
+template <auto KERN>
+hipError_t allow_lds(int bytes) {
+    static bool done[64] = {};
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!done[dev]) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(KERN), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        if (e != hipSuccess) return e;
+        done[dev] = true;
+    }
+    return hipSuccess;
+}
+
 template <int D, bool CAUSAL, bool OUT_F32>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
     using T = Tile<D>;
@@ -534,13 +549,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
     const int per_xcd = (total + NXCD - 1) / NXCD;
     const int grid = per_xcd * NXCD;
     auto kern = fwd_bf16_kernel<D, CAUSAL, OUT_F32>;
-    static bool attr_set = false;   // LDS above the default limit needs an explicit opt-in
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    if (hipError_t e = allow_lds<fwd_bf16_kernel<D, CAUSAL, OUT_F32>>(T::LDS); e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(T::THREADS), T::LDS, s, a, num_qt, total, per_xcd);
     return hipGetLastError();
 }
@@ -1029,13 +1038,7 @@ hipError_t launch_p3(const FwdArgs& a, hipStream_t st) {
     const int per_xcd = (total + NXCD - 1) / NXCD;
     const int grid = per_xcd * NXCD;
     auto kern = fwd_p3_kernel<NW, CAUSAL, OUT_F32>;
-    static bool attr_set = false;   // LDS above the default limit needs an explicit opt-in
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    if (hipError_t e = allow_lds<fwd_p3_kernel<NW, CAUSAL, OUT_F32>>(T::LDS); e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(T::THREADS), T::LDS, st, a, num_qt, total, per_xcd);
     return hipGetLastError();
 }
