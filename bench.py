@@ -13,7 +13,9 @@ resident in HBM before the timed region.  Prints ONE JSON line.
 causal block counted as N^2/2) over the step time.  The `roofline` object covers the dominant kernel (the
 forward launches), timed with HIP events that the library records on the stream the kernels run on.
 `merge` times attn_merge on its own, in place on fp32 partials of the workload's shape (the operation the
-chunked step fuses into its forward launches), against the HBM peak.  `cpu_baseline` times the fp64 CPU
+chunked step fuses into its forward launches), against the HBM peak.  `streamed` runs the same chunked step
+with K and V in page-locked host memory (attn_fwd_streamed): host-to-device GB/s of the chunk copies and how
+much of the shorter of copies and computation the overlap hides.  `cpu_baseline` times the fp64 CPU
 oracle on a bounded sample of the same workload on this host's cores.
 """
 from __future__ import annotations
@@ -70,6 +72,51 @@ def time_merge(w, reps: int):
     n, ms = A.timing_read()["merge"]
     del oa, ob, la, lb
     return ms / max(n, 1)
+
+
+def time_streamed(w, q, k, v, steps: int, compute_ms: float):
+    """The same chunked step with K and V in page-locked host memory (attn_fwd_streamed): chunk p+1 is copied
+    to the device on a second stream while chunk p computes.  Times the step with events on the compute
+    stream, and the chunk copies with the library's events on the copy stream; the overlap efficiency is
+    max(device-resident step, copies alone) over the streamed step (1.0 = the shorter one fully hidden)."""
+    import torch
+
+    import exact_blockwise_attention_fwd_amd as A
+
+    kh, vh = k.cpu().pin_memory(), v.cpu().pin_memory()
+    ws = torch.empty(A.streamed_workspace_bytes(w.B, w.H, w.N_q, w.N_kv, w.d, w.chunks, q.dtype), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N_q), dtype=torch.float32, device="cuda")
+    cs = torch.cuda.Stream()
+
+    def step():
+        A.fwd_streamed(q, kh, vh, w.chunks, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=ws,
+                       copy_stream=cs)
+
+    step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    A.timing_enable(True)
+    A.timing_read()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    A.timing_enable(False)
+    t = A.timing_read()
+    ms = e0.elapsed_time(e1) / steps
+    ncopy, copy_ms = t["copy"]
+    copy_ms /= steps
+    nbytes = 2 * k.numel() * k.element_size()      # every key and value row crosses once per step
+    del kh, vh, ws, o, lse
+    return {"what": "K and V in pinned host memory, chunk p+1 copied on a second stream while chunk p computes",
+            "ms_per_step": round(ms, 4), "copies_per_step": ncopy / steps, "copy_ms_per_step": round(copy_ms, 4),
+            "h2d_gbs": round(nbytes / (copy_ms * 1e-3) / 1e9, 2) if copy_ms > 0 else None,
+            "device_resident_ms_per_step": round(compute_ms, 4),
+            "overlap_efficiency": round(max(compute_ms, copy_ms) / ms, 4)}
 
 
 def cpu_baseline(w, seconds: float):
@@ -163,6 +210,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ring_share_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-streamed", action="store_true", help="skip the host-streamed variant of the chunked step")
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (practical HBM ceiling; also the "
@@ -270,10 +318,15 @@ def main():
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": None if fwd_tflops is None else round(fwd_tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": recorded_traffic(w)},
+        "streamed": None,
         "cpu_baseline": None,
     }
     if w.dtype != "bf16":
         out["roofline"]["bound"] = "alu"
+    if w.chunks > 1 and not args.no_streamed:
+        log("timing the host-streamed chunked step")
+        out["streamed"] = time_streamed(w, q, k, v, max(2, min(args.steps, 5)), ms)
+        log(f"streamed: {out['streamed']}")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -9,6 +9,7 @@ streams.  If the library has not been built, every call raises (there is no fall
     o, lse = fwd_chunked(q, k, v, chunks=8, causal=True)
     o, lse = merge(o_a, lse_a, o_b, lse_b)
     o, lse = fwd_acc(q, k, v, o_acc, lse_acc, causal_offset=..., key_range=(lo, hi))   # fold a key range in
+    o, lse = fwd_streamed(q, k_host, v_host, chunks=8, causal=True)  # k, v in pinned host memory
 """
 from __future__ import annotations
 
@@ -48,14 +49,17 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_chunked_workspace_bytes.argtypes = [i, i, i, i, i]
     L.attn_fwd_chunked_workspace_bytes.restype = sz
     L.attn_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp]
+    L.attn_fwd_streamed_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    L.attn_fwd_streamed_workspace_bytes.restype = sz
+    L.attn_fwd_streamed.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp, vp]
     L.attn_strerror.argtypes = [i]
     L.attn_strerror.restype = ctypes.c_char_p
     L.attn_last_error.argtypes = []
     L.attn_last_error.restype = ctypes.c_char_p
     L.attn_timing_enable.argtypes = [i]
     L.attn_timing_read.argtypes = [ctypes.POINTER(ll), ctypes.POINTER(ctypes.c_double)]
-    for name in ("attn_fwd", "attn_fwd_ex", "attn_fwd_acc", "attn_merge", "attn_fwd_chunked", "attn_timing_enable",
-                 "attn_timing_read"):
+    for name in ("attn_fwd", "attn_fwd_ex", "attn_fwd_acc", "attn_merge", "attn_fwd_chunked", "attn_fwd_streamed",
+                 "attn_timing_enable", "attn_timing_read"):
         getattr(L, name).restype = i
     _lib = L
     return L
@@ -206,13 +210,47 @@ def fwd_chunked(q, k, v, chunks: int, causal: bool = False, scale: float | None 
     return out, lse
 
 
+def streamed_workspace_bytes(B: int, H: int, N_q: int, N_kv: int, d: int, chunks: int, dtype) -> int:
+    return int(lib().attn_fwd_streamed_workspace_bytes(B, H, N_q, N_kv, d, chunks, _dtype_code(
+        __import__("torch").empty(0, dtype=dtype))))
+
+
+def fwd_streamed(q, k_host, v_host, chunks: int, causal: bool = False, scale: float | None = None, out=None,
+                 lse=None, workspace=None, copy_stream=None):
+    """fwd_chunked with k and v in host memory ([B,H,N_kv,d] CPU tensors, pinned for overlap): chunk p+1 is
+    copied to the device on `copy_stream` (a torch stream other than the current one) while chunk p computes."""
+    import torch
+    _need(q, "q")
+    for t, n in ((k_host, "k_host"), (v_host, "v_host")):
+        if t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous host tensor")
+        if t.dtype != q.dtype:
+            raise TypeError(f"{n} must have q's dtype")
+    B, H, N_q, d = q.shape
+    N_kv = k_host.shape[2]
+    dt = _dtype_code(q)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    need = streamed_workspace_bytes(B, H, N_q, N_kv, d, chunks, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if copy_stream is None:
+        copy_stream = torch.cuda.Stream(device=q.device)
+    _check(lib().attn_fwd_streamed(q.data_ptr(), k_host.data_ptr(), v_host.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr(), B, H, N_q, N_kv, d, int(causal), scale, int(chunks), dt,
+                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q),
+                                   ctypes.c_void_p(copy_stream.cuda_stream)), "attn_fwd_streamed")
+    return out, lse
+
+
 def timing_enable(on: bool = True):
     _check(lib().attn_timing_enable(int(on)), "attn_timing_enable")
 
 
 def timing_read():
-    """{'fwd': (launches, total_ms), 'merge': (launches, total_ms)} since the last read."""
-    counts = (ctypes.c_longlong * 2)()
-    ms = (ctypes.c_double * 2)()
+    """{'fwd': (launches, total_ms), 'merge': (...), 'copy': (chunk copies, total_ms)} since the last read."""
+    counts = (ctypes.c_longlong * 3)()
+    ms = (ctypes.c_double * 3)()
     _check(lib().attn_timing_read(counts, ms), "attn_timing_read")
-    return {"fwd": (counts[0], ms[0]), "merge": (counts[1], ms[1])}
+    return {"fwd": (counts[0], ms[0]), "merge": (counts[1], ms[1]), "copy": (counts[2], ms[2])}

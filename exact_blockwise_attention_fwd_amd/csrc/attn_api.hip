@@ -57,6 +57,44 @@ hipEvent_t take_event() {
     return e;
 }
 
+// Synchronisation events of attn_fwd_streamed, four per call (two "copied", two "done").  A set goes back to
+// the pool with the event that completes last; it is handed out again only once that event has completed,
+// so no pending wait or record of an earlier call can see it re-recorded.
+struct EventQuad {
+    hipEvent_t e[4];
+    hipEvent_t last;
+};
+std::mutex g_quad_mu;
+std::vector<EventQuad*> g_quads;
+
+EventQuad* take_quad() {
+    {
+        std::lock_guard<std::mutex> g(g_quad_mu);
+        for (size_t i = 0; i < g_quads.size(); ++i) {
+            EventQuad* q = g_quads[i];
+            if (!q->last || hipEventQuery(q->last) == hipSuccess) {
+                g_quads.erase(g_quads.begin() + i);
+                return q;
+            }
+        }
+    }
+    EventQuad* q = new EventQuad{};
+    for (int k = 0; k < 4; ++k) {
+        if (hipEventCreateWithFlags(&q->e[k], hipEventDisableTiming) != hipSuccess) {
+            for (int j = 0; j < k; ++j) hipEventDestroy(q->e[j]);
+            delete q;
+            return nullptr;
+        }
+    }
+    return q;
+}
+
+void give_quad(EventQuad* q, hipEvent_t last) {
+    q->last = last;
+    std::lock_guard<std::mutex> g(g_quad_mu);
+    g_quads.push_back(q);
+}
+
 // Runs one launch with optional timing and debug synchronisation; maps HIP failures to ATTN_ERR_HIP.
 template <class F>
 int run(int kind, hipStream_t s, const char* what, F&& launch) {
@@ -377,26 +415,130 @@ int attn_fwd_chunked(const void* Q, const void* K, const void* V, void* O, float
     return ATTN_OK;
 }
 
+size_t attn_fwd_streamed_workspace_bytes(int B, int H, int N_q, int N_kv, int d, int P, attn_dtype dtype) {
+    if (B < 1 || H < 1 || N_q < 1 || N_kv < 1 || d < 1 || P < 1 || !valid_dtype(dtype)) return 0;
+    const size_t rows = (size_t)B * H * N_q;
+    const size_t cmax = ((size_t)N_kv + P - 1) / P;   // the longest chunk
+    const size_t slot = (size_t)B * H * cmax * d * esize(dtype);
+    return align256(rows * d * sizeof(float)) + align256(rows * sizeof(float)) + 4 * align256(slot);
+}
+
+int attn_fwd_streamed(const void* Q, const void* K_host, const void* V_host, void* O, float* LSE, int B, int H,
+                      int N_q, int N_kv, int d, int causal, float scale, int P, attn_dtype dtype, void* workspace,
+                      size_t workspace_bytes, void* hip_stream, void* copy_stream) {
+    g_last_error.clear();
+    FwdCheck c;
+    int st = check_fwd(Q, K_host, V_host, O, LSE, B, H, N_q, N_kv, d, scale, 0, dtype, dtype, &c);
+    if (st) return st;
+    if (P < 1) return fail(ATTN_ERR_BAD_SHAPE, "P must be >= 1 (got %d)", P);
+    if (hip_stream == copy_stream) return fail(ATTN_ERR_BAD_ALIAS, "the copy stream must differ from the compute stream");
+    const size_t need = attn_fwd_streamed_workspace_bytes(B, H, N_q, N_kv, d, P, dtype);
+    if (!workspace || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+    if (((uintptr_t)workspace & 255) != 0) return fail(ATTN_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+    const void* others[5] = {Q, K_host, V_host, O, LSE};
+    const size_t other_n[5] = {c.q_bytes, c.kv_bytes, c.kv_bytes, c.o_bytes, c.lse_bytes};
+    for (int i = 0; i < 5; ++i)
+        if (overlap(workspace, need, others[i], other_n[i]))
+            return fail(ATTN_ERR_BAD_ALIAS, "workspace overlaps Q, K, V, O or LSE");
+
+    hipStream_t s = (hipStream_t)hip_stream, cs = (hipStream_t)copy_stream;
+    const long long offset = (long long)N_kv - N_q;
+    // the chunks of attn_fwd_chunked with the same P, in the same order
+    std::vector<int> live;
+    for (int p = 0; p < P; ++p) {
+        const long long lo = (long long)p * N_kv / P, hi = (long long)(p + 1) * N_kv / P;
+        if (hi == lo) continue;
+        if (causal && (long long)N_q - 1 + offset - lo < 0) continue;
+        live.push_back(p);
+    }
+    if (live.empty()) live.push_back(0);
+    const size_t rows = (size_t)B * H * N_q, es = esize(dtype);
+    const size_t cmax = ((size_t)N_kv + P - 1) / P, slot = align256((size_t)B * H * cmax * d * es);
+    char* ws = static_cast<char*>(workspace);
+    float* o_acc = reinterpret_cast<float*>(ws);
+    float* lse_acc = reinterpret_cast<float*>(ws + align256(rows * d * sizeof(float)));
+    char* slots = ws + align256(rows * d * sizeof(float)) + align256(rows * sizeof(float));
+    char* kslot[2] = {slots, slots + 2 * slot};
+    char* vslot[2] = {slots + slot, slots + 3 * slot};
+
+    // copied[b]: slot b holds its chunk; done[b]: the kernel reading slot b has finished
+    EventQuad* ev = take_quad();
+    if (!ev) return fail(ATTN_ERR_HIP, "attn_fwd_streamed: hipEventCreate failed");
+    hipEvent_t* copied = ev->e;
+    hipEvent_t* done = ev->e + 2;
+    const size_t n = live.size();
+    auto bounds = [&](size_t i, long long& lo, long long& hi) {
+        lo = (long long)live[i] * N_kv / P;
+        hi = (long long)(live[i] + 1) * N_kv / P;
+    };
+    auto copy = [&](size_t i) -> int {   // chunk i into slot i % 2, once the kernel of chunk i-2 is done with it
+        const int b = (int)(i & 1);
+        long long lo, hi;
+        bounds(i, lo, hi);
+        const size_t row = (size_t)(hi - lo) * d * es, pitch = (size_t)N_kv * d * es;
+        if (i >= 2 && hipStreamWaitEvent(cs, done[b], 0) != hipSuccess)
+            return fail(ATTN_ERR_HIP, "attn_fwd_streamed: hipStreamWaitEvent failed");
+        return run(2, cs, "attn_fwd_streamed copy", [&] {
+            hipError_t e = hipMemcpy2DAsync(kslot[b], row, static_cast<const char*>(K_host) + lo * d * es, pitch, row,
+                                            (size_t)B * H, hipMemcpyDefault, cs);
+            if (e == hipSuccess)
+                e = hipMemcpy2DAsync(vslot[b], row, static_cast<const char*>(V_host) + lo * d * es, pitch, row,
+                                     (size_t)B * H, hipMemcpyDefault, cs);
+            if (e == hipSuccess) e = hipEventRecord(copied[b], cs);
+            return e;
+        });
+    };
+    // chunk i from slot i % 2 (rows packed: head stride = chunk length * d), folded as in attn_fwd_chunked
+    auto compute = [&](size_t i) -> int {
+        const int b = (int)(i & 1);
+        long long lo, hi;
+        bounds(i, lo, hi);
+        if (hipStreamWaitEvent(s, copied[b], 0) != hipSuccess)
+            return fail(ATTN_ERR_HIP, "attn_fwd_streamed: hipStreamWaitEvent failed");
+        const int len = (int)(hi - lo);
+        const bool first = i == 0, last = i + 1 == n;
+        void* o = last ? O : (void*)o_acc;
+        float* l = last ? LSE : lse_acc;
+        const attn_dtype ot = last ? dtype : ATTN_F32;
+        int r = launch_fwd(Q, kslot[b], vslot[b], o, l, B, H, N_q, len, d, causal, scale, offset - lo,
+                           (long long)len * d, dtype, ot, s, first ? nullptr : o_acc, first ? nullptr : lse_acc);
+        if (r) return r;
+        if (hipEventRecord(done[b], s) != hipSuccess) return fail(ATTN_ERR_HIP, "attn_fwd_streamed: hipEventRecord failed");
+        return ATTN_OK;
+    };
+    st = copy(0);
+    if (!st && n > 1) st = copy(1);
+    for (size_t i = 0; i < n && !st; ++i) {
+        st = compute(i);
+        if (!st && i + 2 < n) st = copy(i + 2);
+    }
+    give_quad(ev, done[(n - 1) & 1]);
+    return st;
+}
+
 int attn_timing_enable(int on) {
     std::lock_guard<std::mutex> g(g_timing_mu);
     g_timing_on = on != 0;
     return ATTN_OK;
 }
 
-int attn_timing_read(long long counts[2], double total_ms[2]) {
+int attn_timing_read(long long counts[3], double total_ms[3]) {
     std::vector<Timed> recs;
     {
         std::lock_guard<std::mutex> g(g_timing_mu);
         recs.swap(g_timed);
     }
-    counts[0] = counts[1] = 0;
-    total_ms[0] = total_ms[1] = 0.0;
+    for (int k = 0; k < 3; ++k) {
+        counts[k] = 0;
+        total_ms[k] = 0.0;
+    }
     int st = ATTN_OK;
     for (const Timed& r : recs) {
         float ms = 0.f;
         if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) {
             st = fail(ATTN_ERR_HIP, "attn_timing_read: event query failed");
-        } else if (r.kind == 0 || r.kind == 1) {
+        } else if (r.kind >= 0 && r.kind < 3) {
             counts[r.kind] += 1;
             total_ms[r.kind] += ms;
         }

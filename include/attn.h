@@ -138,6 +138,36 @@ int attn_fwd_chunked(const void* Q, const void* K, const void* V, void* O, float
                      int B, int H, int N_q, int N_kv, int d, int causal, float scale, int P,
                      attn_dtype dtype, void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/*
+ * attn_fwd_streamed_workspace_bytes - device workspace attn_fwd_streamed needs: the fp32 partial output
+ * [B,H,N_q,d] and lse [B,H,N_q] of attn_fwd_chunked, plus two staging slots, each holding the K and the V
+ * rows of one chunk for every (b, h) ([B*H, ceil(N_kv/P), d] in `dtype`); every piece 256-byte aligned.
+ * Returns 0 for invalid arguments (attn_fwd_streamed reports those).
+ */
+size_t attn_fwd_streamed_workspace_bytes(int B, int H, int N_q, int N_kv, int d, int P, attn_dtype dtype);
+
+/*
+ * attn_fwd_streamed - attn_fwd_chunked with K and V in host memory: the chunks are copied to the device
+ * one after another on `copy_stream` into two staging slots of the workspace, and chunk p+1 is copied
+ * while chunk p is attended on `hip_stream`.  Q, O, LSE and the workspace are device memory; K_host and
+ * V_host are host memory laid out [B,H,N_kv,d] (page-locked, e.g. from hipHostMalloc, for the copies to
+ * overlap the computation; pageable memory gives the same result, serialised).  The chunks, their order,
+ * the skipped chunks and the kernels are those of attn_fwd_chunked with the same P, so O and LSE equal its
+ * result bit for bit.  Every launch and copy is enqueued and the call returns without synchronising;
+ * `hip_stream` waits for each chunk's copy, and when its work is done every copy is done.  The caller keeps
+ * K_host, V_host and the workspace alive until then.  The two streams must differ (NULL is the
+ * default stream; a non-blocking copy stream keeps the copies independent of it).
+ * Errors: those of attn_fwd_chunked (the workspace must not overlap Q, O or LSE), ATTN_ERR_BAD_ALIAS for equal
+ * streams, ATTN_ERR_HIP for a failed copy, event or launch (work enqueued before it stays enqueued).
+ * Source: "Ring Attention with Blockwise Parallel Transformers" explainer, section 3 (the next block's keys
+ * and values arrive while the current block is computed) and section 4 (no added time when a transfer is
+ * shorter than a block's computation).
+ */
+int attn_fwd_streamed(const void* Q, const void* K_host, const void* V_host, void* O, float* LSE,
+                      int B, int H, int N_q, int N_kv, int d, int causal, float scale, int P,
+                      attn_dtype dtype, void* workspace, size_t workspace_bytes, void* hip_stream,
+                      void* copy_stream);
+
 /* attn_strerror - a static string naming a status code. */
 const char* attn_strerror(int status);
 
@@ -145,14 +175,15 @@ const char* attn_strerror(int status);
 const char* attn_last_error(void);
 
 /*
- * Launch timing.  attn_timing_enable(1) makes every kernel launch of the library record a pair of HIP
- * events on its stream (kind 0 = attention forward kernel, 1 = merge kernel); attn_timing_read
- * synchronises those events, returns per-kind launch counts and summed durations in milliseconds, and
- * clears the record.  attn_timing_enable(0) stops recording.  Used by the benchmark to time the kernels
- * on the stream they run on; off by default.  Returns ATTN_ERR_HIP if an event call fails.
+ * Launch timing.  attn_timing_enable(1) makes every kernel launch and chunk copy of the library record a
+ * pair of HIP events on its stream (kind 0 = attention forward kernel, 1 = merge kernel, 2 = the K and V
+ * copy of one chunk in attn_fwd_streamed); attn_timing_read synchronises those events, returns per-kind
+ * counts and summed durations in milliseconds (arrays of 3), and clears the record.  attn_timing_enable(0)
+ * stops recording.  Used by the benchmark to time the work on the stream it runs on; off by default.
+ * Returns ATTN_ERR_HIP if an event call fails.
  */
 int attn_timing_enable(int on);
-int attn_timing_read(long long counts[2], double total_ms[2]);
+int attn_timing_read(long long counts[3], double total_ms[3]);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,8 @@ def test_library_exports_every_declared_symbol():
     lib = A.lib()
     names = declared_functions()
     assert {"attn_fwd", "attn_fwd_ex", "attn_fwd_acc", "attn_merge", "attn_fwd_chunked", "attn_fwd_chunked_workspace_bytes",
-            "attn_strerror", "attn_last_error", "attn_timing_enable", "attn_timing_read"} <= set(names)
+            "attn_fwd_streamed", "attn_fwd_streamed_workspace_bytes", "attn_strerror", "attn_last_error",
+            "attn_timing_enable", "attn_timing_read"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in attn.h but not exported"
 
@@ -62,6 +63,12 @@ def fwd_acc(*, q=P[0], k=P[1], v=P[2], oa=P[5], la=P[6], o=P[3], lse=P[4], B=1, 
 
 def chunked(*, o=P[3], lse=P[4], P_=4, ws=P[6], ws_n=1 << 40, d=64, dtype=A.ATTN_BF16, N_q=8, N_kv=8):
     return A.lib().attn_fwd_chunked(P[0], P[1], P[2], o, lse, 1, 2, N_q, N_kv, d, 0, 0.125, P_, dtype, ws, ws_n, None)
+
+
+def streamed(*, o=P[3], lse=P[4], P_=4, ws=P[6], ws_n=1 << 40, s1=P[0], s2=P[1], d=64, N_kv=8):
+    # the stream handles are never used: every case here fails validation first
+    return A.lib().attn_fwd_streamed(P[0], P[1], P[2], o, lse, 1, 2, 8, N_kv, d, 0, 0.125, P_, A.ATTN_BF16, ws, ws_n,
+                                     s1, s2)
 
 
 def last_error():
@@ -142,6 +149,30 @@ def test_workspace_formula():
     assert f(0, 1, 1, 64, 2) == 0 and f(1, 1, 1, 64, 0) == 0
 
 
+def test_streamed_workspace_formula():
+    f = A.lib().attn_fwd_streamed_workspace_bytes
+    a256 = lambda x: (x + 255) // 256 * 256
+    rows = 1 * 32 * 16384
+    slot = 1 * 32 * 16384 * 128 * 2                     # 131072 keys in 8 chunks of 16384, bf16
+    assert f(1, 32, 16384, 131072, 128, 8, A.ATTN_BF16) == a256(rows * 512) + a256(rows * 4) + 4 * a256(slot)
+    # ragged chunks: the slots hold the longest one, ceil(10 / 3) = 4 keys
+    assert f(1, 1, 3, 10, 5, 3, A.ATTN_F32) == 256 + 256 + 4 * a256(1 * 4 * 5 * 4)
+    assert f(1, 1, 3, 10, 5, 0, A.ATTN_F32) == 0 and f(1, 1, 3, 10, 5, 2, 7) == 0
+
+
+def test_streamed_validation():
+    need = A.lib().attn_fwd_streamed_workspace_bytes(1, 2, 8, 8, 64, 4, A.ATTN_BF16)
+    assert streamed(P_=0) == 2
+    assert streamed(s1=None, s2=None) == 7                          # the default stream twice
+    assert streamed(s2=P[0]) == 7                                    # the same stream twice
+    assert streamed(ws=None) == 6
+    assert streamed(ws_n=need - 1) == 6
+    assert streamed(ws=ctypes.c_void_p(P[6].value + 16)) == 9
+    assert streamed(ws=P[3]) == 7                                     # workspace over O
+    assert streamed(d=100) == 3
+    assert "workspace" in last_error() or "d = 64" in last_error()
+
+
 def test_last_error_is_per_call():
     assert fwd(scale=math.nan) == 5
     assert "finite" in last_error()
@@ -151,7 +182,7 @@ def test_last_error_is_per_call():
 
 def test_timing_read_without_launches():
     assert A.lib().attn_timing_enable(1) == 0
-    assert A.timing_read() == {"fwd": (0, 0.0), "merge": (0, 0.0)}
+    assert A.timing_read() == {"fwd": (0, 0.0), "merge": (0, 0.0), "copy": (0, 0.0)}
     assert A.lib().attn_timing_enable(0) == 0
 
 

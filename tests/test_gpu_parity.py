@@ -354,3 +354,69 @@ def test_ulysses_share_256k():
     o, lse = A.fwd(q, k, v, causal=True, scale=w.scale)
     torch.cuda.synchronize()
     check_sampled(w, st, o, lse, what="ulysses_share_256k seeded rows")
+
+
+# ------------------------------------------------------------- K and V streamed from host memory (NEXT-2)
+STREAMED = [
+    # B, H, N_q, N_kv, d, causal, dtype, chunk counts
+    (1, 2, 300, 777, 128, True, "bf16", (1, 3, 8)),
+    (1, 2, 1000, 257, 64, True, "bf16", (2, 7)),      # N_q > N_kv: future chunks skipped, empty rows
+    (1, 3, 5, 3, 64, False, "bf16", (5,)),           # more chunks than keys: empty chunks skipped
+    (1, 2, 130, 70, 37, True, "f32", (1, 4)),
+    (2, 1, 200, 300, 64, False, "f32", (3,)),
+]
+
+
+@pytest.mark.parametrize("case", STREAMED, ids=lambda c: "x".join(map(str, c[:5])) + ("c" if c[5] else "n") + c[6])
+def test_streamed_equals_chunked(case):
+    """attn_fwd_streamed (K, V in pinned host memory) gives exactly attn_fwd_chunked's result, and the oracle's."""
+    B, H, N_q, N_kv, d, causal, dt, chunk_counts = case
+    w = W.Workload("streamed", B, H, N_q, N_kv, d, dt, causal, 1, seed=4000 + N_q + d)
+    st, (q, k, v) = make(w)
+    o_ref, l_ref = oracle_full(st, w)
+    kh = k.cpu().pin_memory()
+    vh = v.cpu().pin_memory()
+    for P in chunk_counts:
+        oc, lc = A.fwd_chunked(q, k, v, P, causal=causal, scale=w.scale)
+        o, lse = A.fwd_streamed(q, kh, vh, P, causal=causal, scale=w.scale)
+        torch.cuda.synchronize()
+        err = errors(out_to_f64(o), out_to_f64(lse), o_ref, l_ref)
+        print(w, P, err, flush=True)
+        assert_parity(err, dt, f"streamed P={P}")
+        assert torch.equal(o, oc) and torch.equal(lse, lc), f"streamed != chunked at P={P}"
+
+
+def test_streamed_pageable_and_repeated_calls():
+    """Pageable host memory gives the same result (serialised copies); back-to-back calls of different sizes
+    reuse the library's synchronisation events without interfering."""
+    w = W.Workload("streamed2", 1, 2, 256, 1500, 128, "bf16", True, 1, seed=4100)
+    st, (q, k, v) = make(w)
+    kh, vh = k.cpu(), v.cpu()
+    kp, vp = kh.pin_memory(), vh.pin_memory()
+    oc, lc = A.fwd_chunked(q, k, v, 6, causal=True, scale=w.scale)
+    w2 = W.Workload("streamed3", 1, 1, 64, 200, 128, "bf16", False, 1, seed=4101)
+    st2, (q2, k2, v2) = make(w2)
+    oc2, lc2 = A.fwd_chunked(q2, k2, v2, 3, causal=False, scale=w2.scale)
+    k2h, v2h = k2.cpu().pin_memory(), v2.cpu().pin_memory()
+    outs = []
+    for _ in range(2):
+        outs.append(A.fwd_streamed(q, kp, vp, 6, causal=True, scale=w.scale))
+        outs.append(A.fwd_streamed(q2, k2h, v2h, 3, causal=False, scale=w2.scale))
+    outs.append(A.fwd_streamed(q, kh, vh, 6, causal=True, scale=w.scale))
+    torch.cuda.synchronize()
+    for i, (o, lse) in enumerate(outs):
+        ref = (oc, lc) if i % 2 == 0 else (oc2, lc2)
+        assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1]), f"call {i} differs from the chunked result"
+
+
+def test_streamed_ring_share_full_size():
+    """The ring-share workload (1 GiB of K and V in pinned host memory, 8 chunks) streamed equals the
+    device-resident chunked path bit for bit."""
+    w = W.WORKLOADS["ring_share_128k"]
+    st, (q, k, v) = make(w)
+    kh, vh = k.cpu().pin_memory(), v.cpu().pin_memory()
+    oc, lc = A.fwd_chunked(q, k, v, w.chunks, causal=w.causal, scale=w.scale)
+    o, lse = A.fwd_streamed(q, kh, vh, w.chunks, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, oc) and torch.equal(lse, lc)
+    check_sampled(w, st, o, lse, heads=[(0, 0), (0, 31)], what="ring_share_128k streamed")
