@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 BF16_PEAK_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP64_PEAK_TFLOPS = 78.6        # MI355X fp64 vector: 256 CUs x 2.4 GHz x 128 FLOP/clk/CU
 METRIC = "attn fwd TFLOP/s and % of MI355X bf16 MFMA peak; merge GB/s vs HBM peak"
 
 
@@ -322,7 +323,9 @@ def main():
         "cpu_baseline": None,
     }
     if w.dtype != "bf16":
-        out["roofline"]["bound"] = "alu"
+        # the fp32 kernel forms QK^T in fp64 FMAs (PV in fp32); at half the fp32 rate they set its ALU ceiling
+        out["roofline"].update({"bound": "alu", "peak": FP64_PEAK_TFLOPS,
+                                "frac": None if fwd_tflops is None else round(fwd_tflops / FP64_PEAK_TFLOPS, 4)})
     if w.chunks > 1 and not args.no_streamed:
         log("timing the host-streamed chunked step")
         out["streamed"] = time_streamed(w, q, k, v, max(2, min(args.steps, 5)), ms)
