@@ -96,17 +96,57 @@ def _need(t, name):
         raise ValueError(f"{name} must be contiguous")
 
 
-def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
-    """Exact attention over all keys.  q [B,H,N_q,d], k and v [B,H,N_kv,d] -> (o [B,H,N_q,d], lse fp32)."""
-    import torch
+def _same_shape(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _qkv(q, k, v):
+    """q [B,H,N_q,d]; k and v [B,H,N_kv,d] of q's dtype and device."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n)
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, H, N_q, d], got shape {tuple(q.shape)}")
+    B, H, _, d = q.shape
+    if k.dim() != 4 or k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
+        raise ValueError(f"k must be [B, H, N_kv, d] matching q {tuple(q.shape)}, got {tuple(k.shape)}")
+    _same_shape(v, k.shape, "v")
+    for t, n in ((k, "k"), (v, "v")):
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{n} must have q's dtype and device")
+    return _dtype_code(q)
+
+
+def _out(out, shape, code, device, name):
+    """A new output tensor, or the caller's after checking that it is exactly what the call writes."""
+    import torch
+    if out is None:
+        return torch.empty(tuple(shape), dtype=_torch_dtype(code), device=device)
+    _need(out, name)
+    _same_shape(out, shape, name)
+    if out.dtype != _torch_dtype(code) or out.device != device:
+        raise ValueError(f"{name} must be {_torch_dtype(code)} on {device}, got {out.dtype} on {out.device}")
+    return out
+
+
+def _out_code(out, out_dtype, default: int) -> int:
+    """Output dtype code: the given output tensor's, else out_dtype, else the input's."""
+    import torch
+    if out is not None:
+        if out_dtype is not None and out.dtype != out_dtype:
+            raise ValueError(f"out is {out.dtype} but out_dtype is {out_dtype}")
+        return _dtype_code(out)
+    return default if out_dtype is None else _dtype_code(torch.empty(0, dtype=out_dtype))
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """Exact attention over all keys.  q [B,H,N_q,d], k and v [B,H,N_kv,d] -> (o [B,H,N_q,d], lse fp32)."""
+    dt = _qkv(q, k, v)
     B, H, N_q, d = q.shape
     N_kv = k.shape[2]
-    dt = _dtype_code(q)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    out = _out(out, q.shape, dt, q.device, "out")
+    lse = _out(lse, (B, H, N_q), ATTN_F32, q.device, "lse")
     _check(lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                           B, H, N_q, N_kv, d, int(causal), scale, dt, _stream(q)), "attn_fwd")
     return out, lse
@@ -115,20 +155,17 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
 def fwd_ex(q, k, v, causal: bool = False, scale: float | None = None, causal_offset: int | None = None,
            key_range: tuple[int, int] | None = None, out_dtype=None, out=None, lse=None):
     """Attention of q against keys [lo, hi) of k and v with an explicit causal offset and output dtype."""
-    import torch
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n)
+    dt = _qkv(q, k, v)
     B, H, N_q, d = q.shape
     n_total = k.shape[2]
     lo, hi = key_range if key_range is not None else (0, n_total)
     if not (0 <= lo <= hi <= n_total):
         raise ValueError(f"key_range {key_range} outside [0, {n_total}]")
-    dt = _dtype_code(q)
-    odt = dt if out_dtype is None else _dtype_code(torch.empty(0, dtype=out_dtype))
+    odt = _out_code(out, out_dtype, dt)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     offset = (hi - lo) - N_q if causal_offset is None else int(causal_offset)
-    out = torch.empty((B, H, N_q, d), dtype=_torch_dtype(odt), device=q.device) if out is None else out
-    lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    out = _out(out, q.shape, odt, q.device, "out")
+    lse = _out(lse, (B, H, N_q), ATTN_F32, q.device, "lse")
     es = q.element_size()
     _check(lib().attn_fwd_ex(q.data_ptr(), k.data_ptr() + lo * d * es, v.data_ptr() + lo * d * es,
                              out.data_ptr(), lse.data_ptr(), B, H, N_q, hi - lo, d, int(causal), scale,
@@ -142,23 +179,25 @@ def fwd_acc(q, k, v, o_acc, lse_acc, causal: bool = False, scale: float | None =
     """fwd_ex over keys [lo, hi) merged, in the kernel's epilogue, into the running fp32 partial
     (o_acc, lse_acc).  With out=o_acc and lse=lse_acc (and an fp32 out_dtype) the fold is in place."""
     import torch
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o_acc, "o_acc"), (lse_acc, "lse_acc")):
+    dt = _qkv(q, k, v)
+    for t, n in ((o_acc, "o_acc"), (lse_acc, "lse_acc")):
         _need(t, n)
     B, H, N_q, d = q.shape
     if o_acc.dtype != torch.float32 or lse_acc.dtype != torch.float32:
         raise TypeError("o_acc and lse_acc must be float32")
     if tuple(o_acc.shape) != (B, H, N_q, d) or tuple(lse_acc.shape) != (B, H, N_q):
         raise ValueError("o_acc must be [B, H, N_q, d] and lse_acc [B, H, N_q]")
+    if o_acc.device != q.device or lse_acc.device != q.device:
+        raise ValueError("o_acc and lse_acc must be on q's device")
     n_total = k.shape[2]
     lo, hi = key_range if key_range is not None else (0, n_total)
     if not (0 <= lo <= hi <= n_total):
         raise ValueError(f"key_range {key_range} outside [0, {n_total}]")
-    dt = _dtype_code(q)
-    odt = dt if out_dtype is None else _dtype_code(torch.empty(0, dtype=out_dtype))
+    odt = _out_code(out, out_dtype, dt)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     offset = (hi - lo) - N_q if causal_offset is None else int(causal_offset)
-    out = torch.empty((B, H, N_q, d), dtype=_torch_dtype(odt), device=q.device) if out is None else out
-    lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    out = _out(out, q.shape, odt, q.device, "out")
+    lse = _out(lse, (B, H, N_q), ATTN_F32, q.device, "lse")
     es = q.element_size()
     _check(lib().attn_fwd_acc(q.data_ptr(), k.data_ptr() + lo * d * es, v.data_ptr() + lo * d * es,
                               o_acc.data_ptr(), lse_acc.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N_q,
@@ -172,12 +211,24 @@ def merge(o_a, lse_a, o_b, lse_b, out=None, lse=None, out_dtype=None):
     import torch
     for t, n in ((o_a, "o_a"), (lse_a, "lse_a"), (o_b, "o_b"), (lse_b, "lse_b")):
         _need(t, n)
+    if o_a.dim() < 1 or tuple(o_a.shape[:-1]) != tuple(lse_a.shape):
+        raise ValueError(f"o_a must be lse_a's shape plus d, got {tuple(o_a.shape)} and {tuple(lse_a.shape)}")
+    _same_shape(o_b, o_a.shape, "o_b")
+    _same_shape(lse_b, lse_a.shape, "lse_b")
+    if o_b.dtype != o_a.dtype:
+        raise ValueError("o_a and o_b must have the same dtype")
+    for t, n in ((lse_a, "lse_a"), (lse_b, "lse_b")):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{n} must be float32")
+    for t, n in ((lse_a, "lse_a"), (o_b, "o_b"), (lse_b, "lse_b")):
+        if t.device != o_a.device:
+            raise ValueError(f"{n} must be on o_a's device")
     d = o_a.shape[-1]
     rows = lse_a.numel()
     dt = _dtype_code(o_a)
-    odt = dt if out_dtype is None else _dtype_code(torch.empty(0, dtype=out_dtype))
-    out = torch.empty(o_a.shape, dtype=_torch_dtype(odt), device=o_a.device) if out is None else out
-    lse = torch.empty_like(lse_a) if lse is None else lse
+    odt = _out_code(out, out_dtype, dt)
+    out = _out(out, o_a.shape, odt, o_a.device, "out")
+    lse = _out(lse, lse_a.shape, ATTN_F32, o_a.device, "lse")
     _check(lib().attn_merge(o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(), lse_b.data_ptr(), out.data_ptr(),
                             lse.data_ptr(), rows, d, dt, odt, _stream(o_a)), "attn_merge")
     return out, lse
@@ -191,17 +242,17 @@ def fwd_chunked(q, k, v, chunks: int, causal: bool = False, scale: float | None 
                 workspace=None):
     """Keys cut into `chunks` contiguous chunks, each attended separately and folded through the merge."""
     import torch
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n)
+    dt = _qkv(q, k, v)
     B, H, N_q, d = q.shape
     N_kv = k.shape[2]
-    dt = _dtype_code(q)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    out = _out(out, q.shape, dt, q.device, "out")
+    lse = _out(lse, (B, H, N_q), ATTN_F32, q.device, "lse")
     need = workspace_bytes(B, H, N_q, d, chunks)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif workspace is not None:
+        _need(workspace, "workspace")
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().attn_fwd_chunked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -226,15 +277,21 @@ def fwd_streamed(q, k_host, v_host, chunks: int, causal: bool = False, scale: fl
             raise ValueError(f"{n} must be a contiguous host tensor")
         if t.dtype != q.dtype:
             raise TypeError(f"{n} must have q's dtype")
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, H, N_q, d], got shape {tuple(q.shape)}")
     B, H, N_q, d = q.shape
+    if k_host.dim() != 4 or k_host.shape[0] != B or k_host.shape[1] != H or k_host.shape[3] != d:
+        raise ValueError(f"k_host must be [B, H, N_kv, d] matching q {tuple(q.shape)}, got {tuple(k_host.shape)}")
+    _same_shape(v_host, k_host.shape, "v_host")
     N_kv = k_host.shape[2]
     dt = _dtype_code(q)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    out = _out(out, q.shape, dt, q.device, "out")
+    lse = _out(lse, (B, H, N_q), ATTN_F32, q.device, "lse")
     need = streamed_workspace_bytes(B, H, N_q, N_kv, d, chunks, q.dtype)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace")
     if copy_stream is None:
         copy_stream = torch.cuda.Stream(device=q.device)
     _check(lib().attn_fwd_streamed(q.data_ptr(), k_host.data_ptr(), v_host.data_ptr(), out.data_ptr(),

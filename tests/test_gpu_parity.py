@@ -242,11 +242,12 @@ def test_fwd_acc_empty_partial_is_identity():
 
 
 # ------------------------------------------------------------------------------------------------- merge
-@pytest.mark.parametrize("din,dout,d", [("f32", "f32", 128), ("f32", "bf16", 128), ("bf16", "bf16", 64),
-                                        ("f32", "f32", 37), ("bf16", "f32", 5)])
-def test_merge_vs_oracle(din, dout, d):
-    rng = np.random.default_rng(3000 + d)
-    rows = 3001
+MERGE_CASES = [("f32", "f32", 128), ("f32", "bf16", 128), ("bf16", "bf16", 64), ("bf16", "f32", 128),
+               ("f32", "f32", 4), ("f32", "f32", 96), ("f32", "f32", 256), ("f32", "f32", 260),
+               ("f32", "f32", 37), ("bf16", "f32", 5)]
+
+
+def merge_inputs(rng, rows, d, din):
     oa, ob = rng.standard_normal((rows, d)).astype(np.float32), rng.standard_normal((rows, d)).astype(np.float32)
     la, lb = (rng.standard_normal(rows) * 5).astype(np.float32), (rng.standard_normal(rows) * 5).astype(np.float32)
     la[::7] = -np.inf
@@ -255,6 +256,16 @@ def test_merge_vs_oracle(din, dout, d):
     ob[::11] = 0
     if din == "bf16":
         oa, ob = W.f32_to_bf16_bits(oa), W.f32_to_bf16_bits(ob)
+    return oa, la, ob, lb
+
+
+@pytest.mark.parametrize("din,dout,d", MERGE_CASES)
+def test_merge_vs_oracle(din, dout, d):
+    """Row-per-wave kernel (d a multiple of 4 up to 256: lane groups of 1 to 64 lanes per row, idle lanes
+    at d = 96) and the whole-row workgroup kernel (d = 260, 37, 5); 3001 rows leave a ragged last group."""
+    rng = np.random.default_rng(3000 + d)
+    rows = 3001
+    oa, la, ob, lb = merge_inputs(rng, rows, d, din)
     ref_o, ref_l = oracle.merge(storage_to_f64(oa), la.astype(np.float64), storage_to_f64(ob), lb.astype(np.float64))
     tdt = torch.bfloat16 if dout == "bf16" else torch.float32
     o, lse = A.merge(to_device(oa), to_device(la), to_device(ob), to_device(lb), out_dtype=tdt)
@@ -263,6 +274,85 @@ def test_merge_vs_oracle(din, dout, d):
     tol = 2e-2 if dout == "bf16" else 1e-5
     assert not err["nan"] and err["lse_inf_match"]
     assert err["max_abs"] <= tol and err["lse_abs"] <= 1e-5, err
+
+
+@pytest.mark.parametrize("din,dout,d", [("f32", "f32", 128), ("bf16", "f32", 64)])
+def test_merge_misaligned_buffers(din, dout, d):
+    """Buffers aligned to their element size only: the launch falls back from vector loads."""
+    rng = np.random.default_rng(3050 + d)
+    rows = 1025
+    oa, la, ob, lb = merge_inputs(rng, rows, d, din)
+    ref_o, ref_l = oracle.merge(storage_to_f64(oa), la.astype(np.float64), storage_to_f64(ob), lb.astype(np.float64))
+
+    def shifted(x):   # the same values one element past a 256-byte boundary
+        t = to_device(x)
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
+        buf[1:].copy_(t.reshape(-1))
+        return buf[1:].view(t.shape)
+
+    tdt = torch.bfloat16 if dout == "bf16" else torch.float32
+    out = torch.empty(rows * d + 1, dtype=tdt, device="cuda")[1:].view(rows, d)
+    o, lse = A.merge(shifted(oa), to_device(la), shifted(ob), to_device(lb), out=out)
+    torch.cuda.synchronize()
+    assert o.data_ptr() % 16 != 0
+    err = errors(out_to_f64(o), out_to_f64(lse), ref_o, ref_l)
+    assert not err["nan"] and err["lse_inf_match"]
+    assert err["max_abs"] <= 1e-5 and err["lse_abs"] <= 1e-5, err
+
+
+@pytest.mark.parametrize("dout", ["f32", "bf16"])
+def test_merge_large_streaming(dout):
+    """A merge larger than twice the Infinity Cache takes the non-temporal path (two row groups in flight
+    per lane): in place for fp32 out, fp32 -> bf16 out of place; 524,287 rows leave a ragged last group."""
+    rng = np.random.default_rng(3070)
+    rows, d = 524287, 128
+    oa, la, ob, lb = merge_inputs(rng, rows, d, "f32")
+    ref_o, ref_l = oracle.merge(oa.astype(np.float64), la.astype(np.float64), ob.astype(np.float64),
+                                lb.astype(np.float64))
+    ta, tla = to_device(oa), to_device(la)
+    if dout == "f32":
+        o, lse = A.merge(ta, tla, to_device(ob), to_device(lb), out=ta, lse=tla)
+        assert o.data_ptr() == ta.data_ptr()
+    else:
+        o, lse = A.merge(ta, tla, to_device(ob), to_device(lb), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    err = errors(out_to_f64(o), out_to_f64(lse), ref_o, ref_l)
+    assert not err["nan"] and err["lse_inf_match"]
+    assert err["max_abs"] <= (2e-2 if dout == "bf16" else 1e-5) and err["lse_abs"] <= 1e-5, err
+
+
+def test_binding_checks_caller_buffers():
+    """The binding passes raw pointers on, so it refuses caller tensors whose shape, dtype or device differs
+    from what the call reads or writes; a given output tensor decides the output dtype."""
+    w = W.Workload("bind", 1, 2, 64, 96, 128, "bf16", False, 1, seed=3200)
+    st, (q, k, v) = make(w)
+    bad = [
+        lambda: A.fwd(q, k, v, out=torch.empty(q.shape, dtype=torch.float32, device="cuda")),
+        lambda: A.fwd(q, k, v, lse=torch.empty((1, 2, 63), dtype=torch.float32, device="cuda")),
+        lambda: A.fwd(q, k, v[:, :, :95].contiguous()),
+        lambda: A.fwd(q, k[:, :1].contiguous(), v[:, :1].contiguous()),
+        lambda: A.fwd_ex(q, k, v, out=torch.empty(q.shape, dtype=torch.float32, device="cuda"),
+                         out_dtype=torch.bfloat16),
+        lambda: A.fwd_chunked(q, k, v, 2, workspace=torch.empty(1 << 20, dtype=torch.uint8)),
+    ]
+    oa = torch.zeros((10, 128), dtype=torch.float32, device="cuda")
+    la = torch.zeros(10, dtype=torch.float32, device="cuda")
+    bad += [
+        lambda: A.merge(oa, la, oa.to(torch.bfloat16), la),
+        lambda: A.merge(oa, la, oa[:9].contiguous(), la),
+        lambda: A.merge(oa, la, oa, la, out=torch.empty((10, 64), device="cuda")),
+        lambda: A.merge(oa, la, oa, la.to(torch.float64)),
+    ]
+    for i, call in enumerate(bad):
+        with pytest.raises((ValueError, TypeError)):
+            call()
+            pytest.fail(f"case {i} accepted")
+    # bf16 inputs with an fp32 output tensor and no out_dtype: written as fp32
+    o32 = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    o, _ = A.fwd_ex(q, k, v, out=o32)
+    ref, _ = A.fwd_ex(q, k, v, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert o.data_ptr() == o32.data_ptr() and torch.equal(o32, ref)
 
 
 def test_merge_in_place():
