@@ -184,23 +184,49 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_traffic.txt")
 FWD_SOURCE = os.path.join(ROOT, "exact_blockwise_attention_fwd_amd", "csrc", "attn_fwd_bf16.hip")
 
 
-def recorded_traffic(w):
-    """HBM bytes per forward launch from the counter summary under profiles/ (FETCH_SIZE and WRITE_SIZE,
-    each scaled by what the counter reads for a plain copy of known size), or None when that summary is
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_counters.txt")
+
+
+def recorded_fields(path, w):
+    """The machine-readable `key: value` lines of a counter summary under profiles/, or None when it is
     missing, covers another workload, or was taken on a different forward-kernel source."""
     import hashlib
 
     try:
         fields = {}
-        for line in open(TRAFFIC_FILE):
+        for line in open(path):
             if ":" in line and not line.startswith((" ", "#", "|")):
                 key, val = line.split(":", 1)
                 fields[key.strip()] = val.strip()
         sha = hashlib.sha256(open(FWD_SOURCE, "rb").read()).hexdigest()
         if fields.get("kernel_source_sha256") != sha or fields.get("workload") != w.name:
             return None
-        return float(fields["hbm_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
+        return fields
+    except OSError:
+        return None
+
+
+def recorded_traffic(w):
+    """HBM bytes per forward launch (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a
+    plain copy of known size), or None."""
+    f = recorded_fields(TRAFFIC_FILE, w)
+    try:
+        return None if f is None else float(f["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def recorded_counters(w):
+    """Matrix-core figures of the forward launches from SQ/GRBM counters (mean over the step's launches), or
+    None: the fraction of SIMD cycles the MFMA unit was busy, MFMA FLOP issued per algorithmic FLOP, the
+    fraction of MFMA-busy cycles with a VALU instruction issued beside it, LDS bank-conflict cycles per
+    GUI-active cycle and CU, and the engine clock the GUI-active count implies."""
+    f = recorded_fields(COUNTERS_FILE, w)
+    keys = ("mfma_busy_frac", "mfma_flop_per_algorithmic_flop", "valu_coexec_frac_of_mfma_busy",
+            "lds_bank_conflict_frac", "effective_sclk_ghz")
+    try:
+        return None if f is None else {k: float(f[k]) for k in keys}
+    except (KeyError, ValueError):
         return None
 
 
@@ -282,15 +308,19 @@ def main():
     A.timing_enable(True)
     A.timing_read()
     torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]   # per-step spread
     e0.record(stream)
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         step()
+        marks[i + 1].record(stream)
     e1.record(stream)
     torch.cuda.synchronize()
     A.timing_enable(False)
     kt = A.timing_read()
     total_ms = e0.elapsed_time(e1)
     ms = total_ms / args.steps
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     log(f"timed {args.steps} steps: {ms:.3f} ms/step; kernels {kt}")
 
     flops = w.flops()
@@ -309,6 +339,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N_q": w.N_q, "N_kv": w.N_kv, "d": w.d,
                    "causal": w.causal, "chunks": w.chunks, "scale": w.scale, "parallelism": "single-gpu"},
         "pct_bf16_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
+        "step_ms": {"median": round(per_step[len(per_step) // 2], 4), "min": round(per_step[0], 4),
+                    "max": round(per_step[-1], 4)},
         "fwd_kernel": {"launches_per_step": n_fwd / args.steps, "ms_per_step": fwd_ms / args.steps,
                        "tflops": None if fwd_tflops is None else round(fwd_tflops, 2)},
         "merge": None if merge_gbs is None else {
@@ -319,6 +351,7 @@ def main():
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": None if fwd_tflops is None else round(fwd_tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": recorded_traffic(w)},
+        "counters": recorded_counters(w),
         "streamed": None,
         "cpu_baseline": None,
     }
