@@ -155,6 +155,21 @@ struct FwdCheck {
     long long kv_stride;
 };
 
+// Launch limits of the forward kernels: the grid counts blocks of at least 128 query rows (bf16) or 64
+// (fp32) over every head and must stay below 2^31 workgroups; the bf16 kernels bound each K/V tile load by
+// a 31-bit byte count, so one launch reads fewer than 2^31 bytes of K (and of V) per head.
+int check_launch_limits(int B, int H, int N_q, long long keys_per_launch, int d, int dtype) {
+    const long long rows = dtype == ATTN_BF16 ? 128 : 64;
+    if ((N_q + rows - 1) / rows * (long long)B * H > 0x7fffffffLL - 8)
+        return fail(ATTN_ERR_BAD_SHAPE, "ceil(N_q/%lld)*B*H query blocks exceed 2^31-9", rows);
+    if (dtype == ATTN_BF16 && keys_per_launch * d * 2 > 0x7fffffffLL)
+        return fail(ATTN_ERR_BAD_SHAPE,
+                    "bf16 attention reads at most 2^31-1 bytes of K per head and launch: %lld keys at d = %d "
+                    "exceed %lld (the chunked modes apply this per chunk)",
+                    keys_per_launch, d, 0x7fffffffLL / (2LL * d));
+    return ATTN_OK;
+}
+
 int check_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q,
               int N_kv, int d, float scale, long long kv_head_stride, int in_dtype, int out_dtype,
               FwdCheck* out) {
@@ -279,6 +294,7 @@ int attn_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* LSE
     FwdCheck c;
     int st = check_fwd(Q, K, V, O, LSE, B, H, N_q, N_kv, d, scale, kv_head_stride, in_dtype, out_dtype, &c);
     if (st) return st;
+    if ((st = check_launch_limits(B, H, N_q, N_kv, d, in_dtype))) return st;
     return launch_fwd(Q, K, V, O, LSE, B, H, N_q, N_kv, d, causal, scale, causal_offset, c.kv_stride, in_dtype,
                       out_dtype, (hipStream_t)hip_stream);
 }
@@ -297,6 +313,7 @@ int attn_fwd_acc(const void* Q, const void* K, const void* V, const float* O_acc
     FwdCheck c;
     int st = check_fwd(Q, K, V, O, LSE, B, H, N_q, N_kv, d, scale, kv_head_stride, in_dtype, out_dtype, &c);
     if (st) return st;
+    if ((st = check_launch_limits(B, H, N_q, N_kv, d, in_dtype))) return st;
     const size_t acc_bytes = c.lse_bytes * (size_t)d;   // fp32 [B,H,N_q,d]
     if ((((uintptr_t)O_acc | (uintptr_t)lse_acc) & 3) != 0 || (in_dtype == ATTN_BF16 && !aligned16(O_acc)))
         return fail(ATTN_ERR_MISALIGNED, "O_acc must be 16-byte (bf16 inputs) or 4-byte aligned, lse_acc 4-byte");
@@ -366,6 +383,7 @@ int attn_fwd_chunked(const void* Q, const void* K, const void* V, void* O, float
     int st = check_fwd(Q, K, V, O, LSE, B, H, N_q, N_kv, d, scale, 0, dtype, dtype, &c);
     if (st) return st;
     if (P < 1) return fail(ATTN_ERR_BAD_SHAPE, "P must be >= 1 (got %d)", P);
+    if ((st = check_launch_limits(B, H, N_q, ((long long)N_kv + P - 1) / P, d, dtype))) return st;
     hipStream_t s = (hipStream_t)hip_stream;
     const long long offset = (long long)N_kv - N_q;
     if (P == 1)
@@ -431,6 +449,7 @@ int attn_fwd_streamed(const void* Q, const void* K_host, const void* V_host, voi
     int st = check_fwd(Q, K_host, V_host, O, LSE, B, H, N_q, N_kv, d, scale, 0, dtype, dtype, &c);
     if (st) return st;
     if (P < 1) return fail(ATTN_ERR_BAD_SHAPE, "P must be >= 1 (got %d)", P);
+    if ((st = check_launch_limits(B, H, N_q, ((long long)N_kv + P - 1) / P, d, dtype))) return st;
     if (hip_stream == copy_stream) return fail(ATTN_ERR_BAD_ALIAS, "the copy stream must differ from the compute stream");
     const size_t need = attn_fwd_streamed_workspace_bytes(B, H, N_q, N_kv, d, P, dtype);
     if (!workspace || workspace_bytes < need)

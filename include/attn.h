@@ -49,7 +49,11 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
 typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL_PTR = 1,           /* a required pointer is NULL */
-    ATTN_ERR_BAD_SHAPE = 2,          /* B, H, N_q, N_kv, rows or P out of range, or a stride too small */
+    ATTN_ERR_BAD_SHAPE = 2,          /* B, H, N_q, N_kv, rows or P out of range, or a stride too small.
+                                        Launch limits: ceil(N_q/128)*B*H (bf16) or ceil(N_q/64)*B*H (fp32)
+                                        below 2^31-8; bf16 K of one head and launch below 2^31 bytes, i.e.
+                                        N_kv <= 8,388,607 at d = 128 and 16,777,215 at d = 64 (in the
+                                        chunked modes per chunk: ceil(N_kv/P)) */
     ATTN_ERR_UNSUPPORTED_D = 3,      /* head dimension not supported for this dtype */
     ATTN_ERR_BAD_DTYPE = 4,          /* unknown dtype or unsupported dtype combination */
     ATTN_ERR_BAD_SCALE = 5,          /* scale is NaN or infinite */

@@ -120,6 +120,29 @@ def test_misaligned():
     assert fwd_ex(stride=8 * 64 + 4) == 9       # bf16 head stride must keep 16-byte alignment
 
 
+def test_launch_limits():
+    """Sizes past the kernels' launch limits are refused as shapes before any HIP call: bf16 K of one head
+    and launch below 2^31 bytes (per chunk in the chunked modes), and fewer than 2^31-8 query blocks."""
+    far = [ctypes.c_void_p((1 << 47) * (i + 1)) for i in range(8)]   # 128 TiB apart: no overlaps
+    kw = dict(q=far[0], k=far[1], v=far[2], o=far[3], lse=far[4])
+    assert fwd(**kw, B=1, H=1, N_q=64, N_kv=8388608, d=128) == 2
+    assert "8388607" in last_error()
+    assert fwd(**kw, B=1, H=1, N_q=64, N_kv=16777216, d=64) == 2
+    assert "16777215" in last_error()
+    assert fwd_ex(**kw, B=1, H=1, N_q=64, N_kv=8388608, d=128) == 2
+    lib = A.lib()
+    # chunked: 2 chunks of 8,388,608 keys are too long, the same keys in 3 chunks would not be
+    assert lib.attn_fwd_chunked(far[0], far[1], far[2], far[3], far[4], 1, 1, 64, 2 * 8388608, 128, 1, 0.1, 2,
+                                A.ATTN_BF16, far[5], 1 << 40, None) == 2
+    assert "per chunk" in last_error()
+    assert lib.attn_fwd_streamed(far[0], far[1], far[2], far[3], far[4], 1, 1, 64, 2 * 8388608, 128, 1, 0.1, 2,
+                                 A.ATTN_BF16, far[5], 1 << 40, far[6], far[7]) == 2
+    # query blocks: ceil(8192/128) * 32768 * 1024 = 2^31 workgroups
+    assert fwd(**kw, B=32768, H=1024, N_q=8192, N_kv=1, d=64) == 2
+    assert "query blocks" in last_error()
+    assert fwd(**kw, B=32768, H=1024, N_q=4096, N_kv=1, d=64, dtype=A.ATTN_F32) == 2
+
+
 def test_merge_validation():
     assert merge(oa=None) == 1
     assert merge(rows=0) == 2 and merge(d=0) == 2
