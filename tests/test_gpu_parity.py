@@ -438,6 +438,17 @@ def test_ring_share_128k_chunked():
     assert (lse - l1).abs().max().item() <= 1e-4
 
 
+def test_max_keys_per_launch():
+    """The largest key count one bf16 d128 launch accepts (2^31-1 bytes of K and of V per head: 8,388,607
+    keys, a ragged last tile), causal with 200 query rows: sampled rows against the oracle."""
+    w = W.Workload("max_keys", 1, 1, 200, 8388607, 128, "bf16", True, 1, seed=4500)
+    st, (q, k, v) = make(w)
+    o, lse = A.fwd(q, k, v, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    del q, k, v
+    check_sampled(w, st, o, lse, what="8,388,607 keys")
+
+
 def test_ulysses_share_256k():
     w = W.WORKLOADS["ulysses_share_256k"]
     st, (q, k, v) = make(w)
