@@ -532,7 +532,10 @@ int attn_fwd_streamed(const void* Q, const void* K_host, const void* V_host, voi
         st = compute(i);
         if (!st && i + 2 < n) st = copy(i + 2);
     }
-    give_quad(ev, done[(n - 1) & 1]);
+    // Compute n-1 waits for the last copy and follows every earlier compute on its stream, so its "done"
+    // event completes after every use of the set.  After a failure some copy may have no compute waiting
+    // for it; that set is never handed out again.
+    if (!st) give_quad(ev, done[(n - 1) & 1]);
     return st;
 }
 
