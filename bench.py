@@ -47,6 +47,30 @@ def merge_bytes(w) -> float:
     return float(rows * (w.d * (4 + 4 + 4) + 12))
 
 
+def time_graph(step, steps: int) -> float:
+    """ms per step of the same step captured once into a HIP graph and replayed `steps` times.  The entry
+    points allocate nothing and never synchronise, so a step is capturable as it stands; the replays drop
+    the host's launch cost, which matters only when a step's kernels are short."""
+    import torch
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def time_merge(w, reps: int):
     """attn_merge in place on fp32 partials [B,H,N_q,d] (seeded values, the empty rows of a causal chunk
     included), timed with the library's own launch events."""
@@ -238,6 +262,7 @@ def main():
     ap.add_argument("--workload", default="ring_share_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-streamed", action="store_true", help="skip the host-streamed variant of the chunked step")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing of the step")
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (practical HBM ceiling; also the "
@@ -352,6 +377,7 @@ def main():
                      "frac": None if fwd_tflops is None else round(fwd_tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": recorded_traffic(w)},
         "counters": recorded_counters(w),
+        "graph": None,
         "streamed": None,
         "cpu_baseline": None,
     }
@@ -359,6 +385,11 @@ def main():
         # the fp32 kernel forms QK^T in fp64 FMAs (PV in fp32); at half the fp32 rate they set its ALU ceiling
         out["roofline"].update({"bound": "alu", "peak": FP64_PEAK_TFLOPS,
                                 "frac": None if fwd_tflops is None else round(fwd_tflops / FP64_PEAK_TFLOPS, 4)})
+    if not args.no_graph:
+        gms = time_graph(step, args.steps)
+        out["graph"] = {"what": "the same step captured once into a HIP graph and replayed", "steps": args.steps,
+                        "ms_per_step": round(gms, 4), "tflops": round(flops / (gms * 1e-3) / 1e12, 2)}
+        log(f"graph replay: {out['graph']}")
     if w.chunks > 1 and not args.no_streamed:
         log("timing the host-streamed chunked step")
         out["streamed"] = time_streamed(w, q, k, v, max(2, min(args.steps, 5)), ms)

@@ -355,6 +355,47 @@ def test_binding_checks_caller_buffers():
     assert o.data_ptr() == o32.data_ptr() and torch.equal(o32, ref)
 
 
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_graph_capture_and_replay(dt, d):
+    """The chunked forward (three folded chunks, causal) and a merge captured into one HIP graph: nothing in
+    them allocates, clears memory or synchronises, so replays equal the eager calls bit for bit.  Each replay
+    runs on fresh inputs copied in by eager work, with synchronisations between replays."""
+    w = W.Workload("graph", 1, 2, 200, 700, d, dt, True, 3, seed=3300 + d)
+    st, (q, k, v) = make(w)
+    o_ref, l_ref = oracle_full(st, w)
+    ws = torch.empty(max(A.workspace_bytes(1, 2, 200, d, 3), 1), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 2, 200), dtype=torch.float32, device="cuda")
+    om = torch.empty((1, 2, 200, d), dtype=torch.float32, device="cuda")
+    lm = torch.empty_like(lse)
+    o32 = torch.empty((1, 2, 200, d), dtype=torch.float32, device="cuda")
+
+    def work():
+        A.fwd_chunked(q, k, v, 3, causal=True, scale=w.scale, out=o, lse=lse, workspace=ws)
+        o32.copy_(o)
+        A.merge(o32, lse, o32, lse, out=om, lse=lm)   # a row merged with itself: same O, lse + ln 2
+
+    work()   # eager, also sets the kernels' LDS attributes before capture
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (o, lse, om, lm)]
+    assert_parity(errors(out_to_f64(o), out_to_f64(lse), o_ref, l_ref), dt, "eager chunked")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            work()
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        for t in (o, lse, om, lm):
+            t.fill_(float("nan"))               # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((o, lse, om, lm), eager):
+            assert torch.equal(got, want), f"replay {rep} differs from the eager result"
+
+
 def test_merge_in_place():
     rng = np.random.default_rng(3100)
     rows, d = 4096, 128
