@@ -45,6 +45,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "attn_internal.h"
@@ -523,17 +524,18 @@ __global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd
     }
 }
 
-// LDS above the default limit needs an explicit opt-in, once per kernel and device.
+// LDS above the default limit needs an explicit opt-in, once per kernel and device.  Threads that race on
+// the first launch may both set the attribute, which is harmless; the flags themselves are atomic.
 template <auto KERN>
 hipError_t allow_lds(int bytes) {
-    static bool done[64] = {};
+    static std::atomic<bool> done[64] = {};
     int dev = 0;
     if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (!done[dev]) {
+    if (!done[dev].load(std::memory_order_acquire)) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(KERN), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
         if (e != hipSuccess) return e;
-        done[dev] = true;
+        done[dev].store(true, std::memory_order_release);
     }
     return hipSuccess;
 }
