@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -266,6 +267,20 @@ int launch_merge(const void* O_a, const float* lse_a, const void* O_b, const flo
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
+
+namespace attn {
+int device_cus() {
+    static std::atomic<int> cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+}  // namespace attn
 
 extern "C" {
 

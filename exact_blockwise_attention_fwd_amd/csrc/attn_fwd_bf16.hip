@@ -1056,16 +1056,8 @@ static int d128_waves(const FwdArgs& a) {
         const int v = atoi(e);
         if (v == 4 || v == 8) return v;
     }
-    static int cus[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (cus[dev] <= 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cus[dev] = n;
-    }
     const long long wide = (long long)((a.n_q + 255) / 256) * a.bh;
-    return wide >= 8LL * cus[dev] ? 8 : 4;
+    return wide >= 8LL * device_cus() ? 8 : 4;
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, bool out_f32, hipStream_t s) {

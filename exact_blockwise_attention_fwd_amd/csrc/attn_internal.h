@@ -43,4 +43,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, bool out_f32, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 
+// Compute units of the current device, queried once per device (256 if the query fails).
+int device_cus();
+
 }  // namespace attn

@@ -152,6 +152,47 @@ def test_d128_both_workgroup_sizes(case, monkeypatch):
         assert torch.equal(a_, b_), "four- and eight-wave workgroups disagree"
 
 
+# The fp32 kernel shares a query row among 4, 8 or 16 lanes, chosen by the launch size (16 only at d > 32);
+# ATTN_F32_LANES_PER_ROW forces one.  Every shape runs through each, chunked (folded partials) and not,
+# against the oracle; the head dimensions cover every template (d <= 32, 64, 128, 256) and both load paths
+# (float4 rows at d % 4 == 0, element loads otherwise).
+F32_SHAPES = [
+    # B, H, N_q, N_kv, d, causal
+    (1, 2, 200, 300, 64, False),
+    (1, 2, 130, 70, 37, True),
+    (1, 1, 64, 64, 256, True),
+    (1, 1, 100, 333, 200, False),
+    (1, 1, 1, 5, 1, False),
+    (2, 2, 100, 100, 128, True),
+    (1, 1, 77, 129, 30, True),
+]
+
+
+@pytest.mark.parametrize("lanes", ["4", "8", "16"])
+@pytest.mark.parametrize("case", F32_SHAPES, ids=lambda c: "x".join(map(str, c[:5])) + ("c" if c[5] else "n"))
+def test_f32_lanes_per_row(case, lanes, monkeypatch):
+    B, H, N_q, N_kv, d, causal = case
+    monkeypatch.setenv("ATTN_F32_LANES_PER_ROW", lanes)
+    w = W.Workload("f32lanes", B, H, N_q, N_kv, d, "f32", causal, 1, seed=3400 + N_q + d)
+    st, (q, k, v) = make(w)
+    o_ref, l_ref = oracle_full(st, w)
+    o, lse = A.fwd(q, k, v, causal=causal, scale=w.scale)
+    oc, lc = A.fwd_chunked(q, k, v, 3, causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert_parity(errors(out_to_f64(o), out_to_f64(lse), o_ref, l_ref), "f32", f"{w} lanes={lanes}")
+    assert_parity(errors(out_to_f64(oc), out_to_f64(lc), o_ref, l_ref), "f32", f"{w} lanes={lanes} 3 chunks")
+
+
+def test_f32_large_launch():
+    """An fp32 launch large enough for four lanes per row on its own (1024 workgroups of 64 rows), with
+    tiles in flight across many steps: sampled rows against the oracle."""
+    w = W.Workload("f32big", 1, 16, 4096, 2048, 64, "f32", True, 1, seed=3500)
+    st, (q, k, v) = make(w)
+    o, lse = A.fwd(q, k, v, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    check_sampled(w, st, o, lse, what="fp32 16 heads x 4096 rows")
+
+
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_unusual_scales(scale, dt):
