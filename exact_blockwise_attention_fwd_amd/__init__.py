@@ -52,6 +52,9 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_streamed_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     L.attn_fwd_streamed_workspace_bytes.restype = sz
     L.attn_fwd_streamed.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp, vp]
+    L.attn_ffn_workspace_bytes.argtypes = [ll, i, ll]
+    L.attn_ffn_workspace_bytes.restype = sz
+    L.attn_ffn_blockwise.argtypes = [vp, vp, vp, vp, vp, vp, ll, i, i, ll, i, vp, sz, vp]
     L.attn_strerror.argtypes = [i]
     L.attn_strerror.restype = ctypes.c_char_p
     L.attn_last_error.argtypes = []
@@ -59,7 +62,7 @@ def lib() -> ctypes.CDLL:
     L.attn_timing_enable.argtypes = [i]
     L.attn_timing_read.argtypes = [ctypes.POINTER(ll), ctypes.POINTER(ctypes.c_double)]
     for name in ("attn_fwd", "attn_fwd_ex", "attn_fwd_acc", "attn_merge", "attn_fwd_chunked", "attn_fwd_streamed",
-                 "attn_timing_enable", "attn_timing_read"):
+                 "attn_ffn_blockwise", "attn_timing_enable", "attn_timing_read"):
         getattr(L, name).restype = i
     _lib = L
     return L
@@ -301,13 +304,60 @@ def fwd_streamed(q, k_host, v_host, chunks: int, causal: bool = False, scale: fl
     return out, lse
 
 
+ATTN_ACT = {"none": 0, "relu": 1, "gelu": 2}
+
+
+def ffn_workspace_bytes(M: int, d_ff: int, block: int) -> int:
+    return int(lib().attn_ffn_workspace_bytes(int(M), int(d_ff), int(block)))
+
+
+def ffn_blockwise(x, w1, b1, w2, b2, block: int | None = None, act: str = "gelu", out=None, workspace=None):
+    """Blockwise feed-forward: act(x W1^T + b1) W2^T + b2 for every row of x [..., d_model] (bf16), the rows
+    taken in contiguous blocks of `block` (default 4096); w1 [d_ff, d_model], w2 [d_model, d_ff] bf16;
+    b1 [d_ff], b2 [d_model] fp32 or None."""
+    import torch
+    for t, n in ((x, "x"), (w1, "w1"), (w2, "w2")):
+        _need(t, n)
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{n} must be bfloat16")
+    d_model = x.shape[-1]
+    d_ff = w1.shape[0]
+    _same_shape(w1, (d_ff, d_model), "w1")
+    _same_shape(w2, (d_model, d_ff), "w2")
+    for t, n, size in ((b1, "b1", d_ff), (b2, "b2", d_model)):
+        if t is not None:
+            _need(t, n)
+            _same_shape(t, (size,), n)
+            if t.dtype != torch.float32:
+                raise TypeError(f"{n} must be float32")
+    for t, n in ((w1, "w1"), (w2, "w2"), (b1, "b1"), (b2, "b2")):
+        if t is not None and t.device != x.device:
+            raise ValueError(f"{n} must be on x's device")
+    if act not in ATTN_ACT:
+        raise ValueError(f"act must be one of {sorted(ATTN_ACT)}")
+    M = x.numel() // d_model
+    block = 4096 if block is None else int(block)
+    out = _out(out, x.shape, ATTN_BF16, x.device, "out")
+    need = ffn_workspace_bytes(M, d_ff, block)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _need(workspace, "workspace")
+    _check(lib().attn_ffn_blockwise(x.data_ptr(), w1.data_ptr(), None if b1 is None else b1.data_ptr(),
+                                    w2.data_ptr(), None if b2 is None else b2.data_ptr(), out.data_ptr(), M, d_model,
+                                    d_ff, block, ATTN_ACT[act], workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), _stream(x)), "attn_ffn_blockwise")
+    return out
+
+
 def timing_enable(on: bool = True):
     _check(lib().attn_timing_enable(int(on)), "attn_timing_enable")
 
 
 def timing_read():
-    """{'fwd': (launches, total_ms), 'merge': (...), 'copy': (chunk copies, total_ms)} since the last read."""
-    counts = (ctypes.c_longlong * 3)()
-    ms = (ctypes.c_double * 3)()
+    """{'fwd': (launches, total_ms), 'merge': (...), 'copy': (chunk copies, total_ms), 'ffn': (GEMM launches,
+    total_ms)} since the last read."""
+    counts = (ctypes.c_longlong * 4)()
+    ms = (ctypes.c_double * 4)()
     _check(lib().attn_timing_read(counts, ms), "attn_timing_read")
-    return {"fwd": (counts[0], ms[0]), "merge": (counts[1], ms[1]), "copy": (counts[2], ms[2])}
+    return {"fwd": (counts[0], ms[0]), "merge": (counts[1], ms[1]), "copy": (counts[2], ms[2]),
+            "ffn": (counts[3], ms[3])}

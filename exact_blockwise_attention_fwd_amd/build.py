@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_api.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_merge.hip"]
+SOURCES = ["attn_api.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_merge.hip", "ffn_bf16.hip"]
 
 # Packed fp32 VALU instructions are switched off for all device code (the compiler would otherwise form
 # them from ordinary float code); the host pass warns that it does not know the feature, which is harmless.

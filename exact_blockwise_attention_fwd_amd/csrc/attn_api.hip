@@ -554,19 +554,72 @@ int attn_fwd_streamed(const void* Q, const void* K_host, const void* V_host, voi
     return st;
 }
 
+size_t attn_ffn_workspace_bytes(long long M, int d_ff, long long block) {
+    if (M < 1 || d_ff < 1 || block < 1) return 0;
+    return align256((size_t)(block < M ? block : M) * d_ff * 2);
+}
+
+int attn_ffn_blockwise(const void* X, const void* W1, const float* b1, const void* W2, const float* b2, void* Y,
+                       long long M, int d_model, int d_ff, long long block, attn_act act, void* workspace,
+                       size_t workspace_bytes, void* hip_stream) {
+    g_last_error.clear();
+    if (!X || !W1 || !W2 || !Y) return fail(ATTN_ERR_NULL_PTR, "X, W1, W2 and Y must be non-NULL");
+    if (M < 1 || block < 1) return fail(ATTN_ERR_BAD_SHAPE, "M and block must be >= 1 (got %lld, %lld)", M, block);
+    if (d_model < 32 || d_ff < 32 || d_model % 32 || d_ff % 32)
+        return fail(ATTN_ERR_UNSUPPORTED_D, "d_model and d_ff must be positive multiples of 32 (got %d, %d)",
+                    d_model, d_ff);
+    if (act != ATTN_ACT_NONE && act != ATTN_ACT_RELU && act != ATTN_ACT_GELU)
+        return fail(ATTN_ERR_BAD_DTYPE, "unknown activation %d", (int)act);
+    const long long rows = block < M ? block : M;
+    const long long lim = 0x7fffffffLL;
+    if (rows * d_ff * 2 > lim || rows * d_model * 2 > lim || (long long)d_ff * d_model * 2 > lim)
+        return fail(ATTN_ERR_BAD_SHAPE,
+                    "a row block (%lld x %d), its hidden block (%lld x %d) and each weight (%d x %d) must stay "
+                    "below 2^31 bytes",
+                    rows, d_model, rows, d_ff, d_ff, d_model);
+    if (M > (1LL << 40) / d_model) return fail(ATTN_ERR_BAD_SHAPE, "M*d_model too large");
+    if (!aligned16(X) || !aligned16(W1) || !aligned16(W2) || !aligned16(Y) ||
+        ((uintptr_t)b1 & 3) || ((uintptr_t)b2 & 3))
+        return fail(ATTN_ERR_MISALIGNED, "X, W1, W2, Y need 16-byte alignment and b1, b2 4-byte alignment");
+    const size_t need = attn_ffn_workspace_bytes(M, d_ff, block);
+    if (!workspace || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+    if (!aligned16(workspace)) return fail(ATTN_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+    const size_t xy = (size_t)M * d_model * 2, w = (size_t)d_ff * d_model * 2;
+    const void* ins[5] = {X, W1, W2, b1, b2};
+    const size_t in_n[5] = {xy, w, w, b1 ? (size_t)d_ff * 4 : 0, b2 ? (size_t)d_model * 4 : 0};
+    for (int i = 0; i < 5; ++i) {
+        if (overlap(Y, xy, ins[i], in_n[i])) return fail(ATTN_ERR_BAD_ALIAS, "Y overlaps an input");
+        if (overlap(workspace, need, ins[i], in_n[i])) return fail(ATTN_ERR_BAD_ALIAS, "workspace overlaps an input");
+    }
+    if (overlap(workspace, need, Y, xy)) return fail(ATTN_ERR_BAD_ALIAS, "workspace overlaps Y");
+
+    hipStream_t s = (hipStream_t)hip_stream;
+    for (long long r0 = 0; r0 < M; r0 += rows) {
+        const int n_rows = (int)(M - r0 < rows ? M - r0 : rows);
+        attn::GemmArgs g1{static_cast<const char*>(X) + (size_t)r0 * d_model * 2, W1, b1, workspace, n_rows, d_ff,
+                          d_model, (int)act};
+        attn::GemmArgs g2{workspace, W2, b2, static_cast<char*>(Y) + (size_t)r0 * d_model * 2, n_rows, d_model,
+                          d_ff, ATTN_ACT_NONE};
+        if (int st = run(3, s, "attn_ffn_blockwise (W1)", [&] { return attn::launch_gemm_nt(g1, s); })) return st;
+        if (int st = run(3, s, "attn_ffn_blockwise (W2)", [&] { return attn::launch_gemm_nt(g2, s); })) return st;
+    }
+    return ATTN_OK;
+}
+
 int attn_timing_enable(int on) {
     std::lock_guard<std::mutex> g(g_timing_mu);
     g_timing_on = on != 0;
     return ATTN_OK;
 }
 
-int attn_timing_read(long long counts[3], double total_ms[3]) {
+int attn_timing_read(long long counts[4], double total_ms[4]) {
     std::vector<Timed> recs;
     {
         std::lock_guard<std::mutex> g(g_timing_mu);
         recs.swap(g_timed);
     }
-    for (int k = 0; k < 3; ++k) {
+    for (int k = 0; k < 4; ++k) {
         counts[k] = 0;
         total_ms[k] = 0.0;
     }
@@ -575,7 +628,7 @@ int attn_timing_read(long long counts[3], double total_ms[3]) {
         float ms = 0.f;
         if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) {
             st = fail(ATTN_ERR_HIP, "attn_timing_read: event query failed");
-        } else if (r.kind >= 0 && r.kind < 3) {
+        } else if (r.kind >= 0 && r.kind < 4) {
             counts[r.kind] += 1;
             total_ms[r.kind] += ms;
         }

@@ -37,11 +37,23 @@ struct MergeArgs {
     int in_bf16, out_bf16;
 };
 
+// One bf16 GEMM of the blockwise feed-forward: C[m][n] = act(sum_k A[m][k] B[n][k] + bias[n]) in bf16, fp32
+// accumulation; A [rows][k] and B [n][k] K-contiguous, C [rows][n]; k and n multiples of 32; bias fp32 or NULL.
+struct GemmArgs {
+    const void* a;
+    const void* b;
+    const float* bias;
+    void* c;
+    int rows, n, k;
+    int act;                // 0 none, 1 ReLU, 2 GELU
+};
+
 // bf16 inputs, fp32 accumulation; d in {64, 128}; O in bf16 or fp32.
 hipError_t launch_fwd_bf16(const FwdArgs& a, bool out_f32, hipStream_t s);
 // fp32 inputs and output; 1 <= d <= 256.
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_gemm_nt(const GemmArgs& g, hipStream_t s);
 
 // Compute units of the current device, queried once per device (256 if the query fails).
 int device_cus();

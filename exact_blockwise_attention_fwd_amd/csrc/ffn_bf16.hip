@@ -1,0 +1,237 @@
+// Blockwise feed-forward on gfx950: FFN(x) = act(x W1^T + b1) W2^T + b2 for every row of a sequence, taken in
+// contiguous row blocks ("Ring Attention with Blockwise Parallel Transformers" explainer, section 3:
+// self-attention and the feedforward applied block by block), so the hidden activations exist for one block
+// at a time.  Each block is two bf16 GEMMs with fp32 accumulation on the matrix cores; bias and activation
+// are applied in the first GEMM's epilogue and the hidden block is stored in bf16, the second GEMM adds its
+// bias in its epilogue.
+//
+// The GEMM is C[m][n] = epi(sum_k A[m][k] B[n][k]) with both operands K-contiguous (activations row-major,
+// weights in the [out, in] layout), which is the layout the MFMA operands want:
+//  * a workgroup computes a 256 x 256 tile of C with 8 waves (two per SIMD); wave w owns rows
+//    64*(w%4) .. +63 and columns 128*(w/4) .. +127, as 2 x 4 blocks of 32 x 32;
+//  * the tile is computed transposed (C^T = B A^T, v_mfma_f32_32x32x16_bf16 with A = B rows and B = A rows)
+//    so that every lane ends with one row m of C and 4-element runs of its columns, which are stored as
+//    8-byte bf16 groups;
+//  * K advances in tiles of 32: A and B tiles (256 rows x 64 bytes each) move HBM -> LDS with
+//    buffer_load_dwordx4 ... lds into a ring of 4 stages, two k-tiles ahead of the one being computed, one
+//    barrier per k-tile; rows past the end of A or B read as zeros (the buffer resource's bound);
+//  * LDS rows are XOR-swizzled in 16-byte units (chunk c of row r sits in slot c ^ ((r >> 2) & 3)) so that
+//    the operand reads of each 16-lane group hit 16 distinct bank groups; the swizzle is applied through
+//    the global chunk each lane fetches;
+//  * workgroups are ordered in groups of 4 row tiles with the column tile varying slowest inside a group,
+//    and each XCD takes a contiguous range of that order, so concurrently running tiles share A and B
+//    tiles in the XCD's L2.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "attn_internal.h"
+
+namespace attn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+constexpr int NXCD = 8;
+constexpr unsigned BUF_RSRC_WORD3 = 0x00020000u;   // raw buffer, 32-bit data format, bounds-checked
+
+constexpr int G_BM = 256, G_BN = 256, G_BK = 32;    // C tile and k-tile
+constexpr int G_NW = 8, G_THREADS = 64 * G_NW;
+constexpr int G_STAGES = 4, G_LEAD = 2;             // LDS ring; k-tiles in flight ahead of the computed one
+constexpr int G_ROW = 2 * G_BK;                     // 64 bytes per LDS row
+constexpr int G_TILE = G_BM * G_ROW;                // 16 KiB per operand tile
+constexpr int G_STAGE = 2 * G_TILE;                 // A tile then B tile
+constexpr int G_LDS = G_STAGES * G_STAGE;           // 128 KiB
+constexpr int G_SEGS = G_TILE / 1024;               // 1 KiB load segments per operand tile
+constexpr int G_SEG_PER_WAVE = G_SEGS / G_NW;       // per operand and k-tile
+constexpr int G_LOADS = 2 * G_SEG_PER_WAVE;         // load instructions per wave and k-tile
+constexpr int G_GROUP_M = 4;
+static_assert(G_SEGS % G_NW == 0 && G_STAGES > G_LEAD, "tiling");
+
+enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2 };
+
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 p = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(unsigned, p);
+}
+
+template <int ACT>
+__device__ __forceinline__ float activate(float x) {
+    if constexpr (ACT == ACT_RELU) return fmaxf(x, 0.f);
+    else if constexpr (ACT == ACT_GELU) return 0.5f * x * (1.f + erff(x * 0.70710678118654752f));
+    else return x;
+}
+
+template <int ACT>
+__global__ __launch_bounds__(G_THREADS, 1) void gemm_nt_kernel(GemmArgs g, int tiles_m, int tiles_n, int total,
+                                                               int per_xcd) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    lds_char* const lds = (lds_char*)smem;
+
+    const int w_hw = blockIdx.x;
+    const int logical = (w_hw % NXCD) * per_xcd + w_hw / NXCD;
+    if (logical >= total) return;
+    const int group = logical / (G_GROUP_M * tiles_n);
+    const int first_m = group * G_GROUP_M;
+    const int gm = min(G_GROUP_M, tiles_m - first_m);
+    const int idx = logical % (G_GROUP_M * tiles_n);
+    const int tm = first_m + idx % gm, tn = idx / gm;
+    const int m0 = tm * G_BM, n0 = tn * G_BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, col = lane & 31;
+    const int K = g.k;
+    const int nk = K / G_BK;
+
+    // ---- loads: this wave fills segments wave and wave + 8 of the A and the B tile of every k-tile.  Lane L
+    // writes LDS row 16*seg + L/4, slot L%4, which must hold chunk (L%4) ^ swz(row) of that row.
+    const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)g.a + (size_t)m0 * K * 2), (short)0, (g.rows - m0) * K * 2, BUF_RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)g.b + (size_t)n0 * K * 2), (short)0, (g.n - n0) * K * 2, BUF_RSRC_WORD3);
+    int voff[G_SEG_PER_WAVE];
+#pragma unroll
+    for (int j = 0; j < G_SEG_PER_WAVE; ++j) {
+        const int row = 16 * (wave + G_NW * j) + lane / 4;
+        voff[j] = row * K * 2 + 16 * ((lane % 4) ^ swz(row));
+    }
+    auto issue = [&](int kt) {
+        lds_char* st = lds + (kt % G_STAGES) * G_STAGE;
+#pragma unroll
+        for (int j = 0; j < G_SEG_PER_WAVE; ++j) {
+            const int seg = wave + G_NW * j;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_void*)(st + seg * 1024), 16, voff[j], kt * G_ROW, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_void*)(st + G_TILE + seg * 1024), 16, voff[j],
+                                                     kt * G_ROW, 0, 0);
+        }
+    };
+
+    // ---- operand reads: row col of a 32-row block, k-chunk 2*ks + h (8 bf16) of the k-tile
+    const int wm0 = 64 * (wave % 4), wn0 = 128 * (wave / 4);
+    int aro[2], bro[4];   // byte offsets within a stage's A / B tile, for ks = 0 (ks = 1 flips chunk bit 1)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const int r = wm0 + 32 * mb + col;
+        aro[mb] = r * G_ROW + 16 * (h ^ swz(r));
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+        const int r = wn0 + 32 * nb + col;
+        bro[nb] = G_TILE + r * G_ROW + 16 * (h ^ swz(r));
+    }
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = f32x16{};
+
+    for (int t = 0; t < G_LEAD && t < nk; ++t) issue(t);
+    for (int kt = 0; kt < nk; ++kt) {
+        // this wave's loads of k-tile kt have landed (the later ones may fly); after the barrier every
+        // wave's have, and every wave is done with the stage that k-tile kt + LEAD overwrites (last read
+        // in iteration kt + LEAD - STAGES < kt)
+        if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F70 | G_LOADS);
+        else __builtin_amdgcn_s_waitcnt(0x0F70);
+        lds_barrier();
+        if (kt + G_LEAD < nk) issue(kt + G_LEAD);
+        const lds_char* st = lds + (kt % G_STAGES) * G_STAGE;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            u32x4 af[2], bf[4];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) af[mb] = *(const lds_u32x4*)(st + (aro[mb] ^ (32 * ks)));
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) bf[nb] = *(const lds_u32x4*)(st + (bro[nb] ^ (32 * ks)));
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+                    acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, bf[nb]), __builtin_bit_cast(bf16x8, af[mb]), acc[nb][mb], 0, 0, 0);
+        }
+    }
+
+    // ---- epilogue: lane holds C[m][n] for m = m0 + wm0 + 32*mb + col and n = n0 + wn0 + 32*nb + 8*q + 4*h + r
+    // (accumulator element 4*q + r); bias, activation, bf16, 8-byte stores of 4 consecutive columns
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const int m = m0 + wm0 + 32 * mb + col;
+        if (m >= g.rows) continue;
+        uint16_t* crow = static_cast<uint16_t*>(g.c) + (size_t)m * g.n;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wn0 + 32 * nb + 8 * q + 4 * h;
+                if (n >= g.n) continue;
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float b = g.bias ? g.bias[n + r] : 0.f;
+                    v[r] = activate<ACT>(acc[nb][mb][4 * q + r] + b);
+                }
+                *reinterpret_cast<u32x2*>(crow + n) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+            }
+        }
+    }
+}
+
+template <auto KERN>
+hipError_t allow_lds(int bytes) {
+    static std::atomic<bool> done[64] = {};
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!done[dev].load(std::memory_order_acquire)) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(KERN), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        if (e != hipSuccess) return e;
+        done[dev].store(true, std::memory_order_release);
+    }
+    return hipSuccess;
+}
+
+template <int ACT>
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
+    const int tiles_m = (g.rows + G_BM - 1) / G_BM, tiles_n = (g.n + G_BN - 1) / G_BN;
+    const int total = tiles_m * tiles_n;
+    const int per_xcd = (total + NXCD - 1) / NXCD;
+    if (hipError_t e = allow_lds<gemm_nt_kernel<ACT>>(G_LDS); e != hipSuccess) return e;
+    hipLaunchKernelGGL(gemm_nt_kernel<ACT>, dim3(per_xcd * NXCD), dim3(G_THREADS), G_LDS, s, g, tiles_m, tiles_n,
+                       total, per_xcd);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_nt(const GemmArgs& g, hipStream_t s) {
+    switch (g.act) {
+        case ACT_RELU: return launch_gemm<ACT_RELU>(g, s);
+        case ACT_GELU: return launch_gemm<ACT_GELU>(g, s);
+        default: return launch_gemm<ACT_NONE>(g, s);
+    }
+}
+
+}  // namespace attn

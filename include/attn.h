@@ -172,6 +172,30 @@ int attn_fwd_streamed(const void* Q, const void* K_host, const void* V_host, voi
                       attn_dtype dtype, void* workspace, size_t workspace_bytes, void* hip_stream,
                       void* copy_stream);
 
+/*
+ * Blockwise feed-forward, the other half of a blockwise transformer block ("Ring Attention with Blockwise
+ * Parallel Transformers" explainer, section 3: the sequence is cut into contiguous blocks and
+ * self-attention and the feedforward are applied block by block).  The page names the standard feedforward
+ * without defining it; this computes, for every row x of X,
+ *     FFN(x) = act(x W1^T + b1) W2^T + b2,     act = GELU (x * Phi(x), the exact erf form) or ReLU,
+ * taking the rows in contiguous blocks of `block` rows (the last one ragged), so the hidden activations
+ * exist for one block at a time, in the caller's workspace.
+ *   X [M, d_model] bf16; W1 [d_ff, d_model] bf16 and W2 [d_model, d_ff] bf16 (the [out, in] layout of a
+ *   linear layer); b1 [d_ff] and b2 [d_model] fp32, or NULL for none; Y [M, d_model] bf16.
+ *   Each block is two bf16 GEMMs with fp32 accumulation on the matrix cores; the hidden block is rounded
+ *   to bf16 between them (bias and activation applied in fp32 before the rounding).
+ *   d_model and d_ff: positive multiples of 32.  A row block, its hidden block and each weight must stay
+ *   below 2^31 bytes.  X, W1, W2, Y and the workspace: 16-byte aligned; b1, b2: 4-byte aligned.
+ *   The workspace holds min(block, M) * d_ff bf16 values (attn_ffn_workspace_bytes); it is overwritten.
+ *   Y must not overlap any input or the workspace.  Enqueued on hip_stream like every call here.
+ */
+typedef enum { ATTN_ACT_NONE = 0, ATTN_ACT_RELU = 1, ATTN_ACT_GELU = 2 } attn_act;
+
+size_t attn_ffn_workspace_bytes(long long M, int d_ff, long long block);
+int attn_ffn_blockwise(const void* X, const void* W1, const float* b1, const void* W2, const float* b2, void* Y,
+                       long long M, int d_model, int d_ff, long long block, attn_act act,
+                       void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* attn_strerror - a static string naming a status code. */
 const char* attn_strerror(int status);
 
@@ -181,13 +205,14 @@ const char* attn_last_error(void);
 /*
  * Launch timing.  attn_timing_enable(1) makes every kernel launch and chunk copy of the library record a
  * pair of HIP events on its stream (kind 0 = attention forward kernel, 1 = merge kernel, 2 = the K and V
- * copy of one chunk in attn_fwd_streamed); attn_timing_read synchronises those events, returns per-kind
- * counts and summed durations in milliseconds (arrays of 3), and clears the record.  attn_timing_enable(0)
+ * copy of one chunk in attn_fwd_streamed, 3 = a GEMM of attn_ffn_blockwise); attn_timing_read synchronises
+ * those events, returns per-kind counts and summed durations in milliseconds (arrays of 4), and clears the
+ * record.  attn_timing_enable(0)
  * stops recording.  Used by the benchmark to time the work on the stream it runs on; off by default.
  * Returns ATTN_ERR_HIP if an event call fails.
  */
 int attn_timing_enable(int on);
-int attn_timing_read(long long counts[3], double total_ms[3]);
+int attn_timing_read(long long counts[4], double total_ms[4]);
 
 #ifdef __cplusplus
 }

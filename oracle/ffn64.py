@@ -9,7 +9,8 @@ block by block.  The pages name the feedforward of a standard Transformer withou
 readings taken here (each listed with its reason in the design notes):
   * the feedforward is the position-wise two-layer network  FFN(x) = act(x W1^T + b1) W2^T + b2  applied
     to every row x of the sequence, with W1 [d_ff, d] and W2 [d, d_ff] in the [out, in] layout;
-  * act is GELU in its exact form x * Phi(x) (Phi the standard normal CDF), or ReLU;
+  * act is GELU in its exact form x * Phi(x) (Phi the standard normal CDF), or ReLU, or none (the two
+    linear layers alone, which the library also offers);
   * the blockwise form applies it to contiguous row blocks of `block` rows, the last one ragged; rows are
     independent, so every block size gives the same result.
 
@@ -36,7 +37,11 @@ def relu(x) -> np.ndarray:
     return np.maximum(_as64(x), 0.0)
 
 
-ACTS = {"gelu": gelu, "relu": relu}
+def identity(x) -> np.ndarray:
+    return _as64(x)
+
+
+ACTS = {"gelu": gelu, "relu": relu, "none": identity}
 
 
 def ffn_rows(x, w1, b1, w2, b2, act: str = "gelu") -> np.ndarray:

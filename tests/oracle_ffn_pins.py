@@ -120,6 +120,8 @@ def check_special_weights(impl, seed=23):
     eye = np.eye(5)
     for act in ("gelu", "relu"):
         _close(impl.ffn_rows(x, eye, None, eye, None, act), impl.ACTS[act](x), 1e-15, f"identity {act}")
+    _close(impl.ffn_rows(x, eye, None, eye, None, "none"), x, 1e-15, "identity weights, no activation")
+    _close(impl.ffn_rows(x, 2 * eye, None, eye / 4, None, "none"), x / 2, 1e-15, "linear layers compose")
     _, w1, b1, _, b2 = _rand(rng, 6, 5, 7)
     _close(impl.ffn_rows(x, w1, b1, np.zeros((5, 7)), b2, "gelu"), np.tile(b2, (6, 1)), 0.0, "W2 = 0")
 

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"attn_fwd", "attn_fwd_ex", "attn_fwd_acc", "attn_merge", "attn_fwd_chunked", "attn_fwd_chunked_workspace_bytes",
             "attn_fwd_streamed", "attn_fwd_streamed_workspace_bytes", "attn_strerror", "attn_last_error",
-            "attn_timing_enable", "attn_timing_read"} <= set(names)
+            "attn_ffn_blockwise", "attn_ffn_workspace_bytes", "attn_timing_enable", "attn_timing_read"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in attn.h but not exported"
 
@@ -203,9 +203,42 @@ def test_last_error_is_per_call():
     assert "d = 64 or 128" in last_error()
 
 
+def ffn(*, x=P[0], w1=P[1], b1=None, w2=P[2], b2=None, y=P[3], M=100, d=64, d_ff=256, block=64, act=2, ws=P[4],
+        ws_n=1 << 40):
+    return A.lib().attn_ffn_blockwise(x, w1, b1, w2, b2, y, M, d, d_ff, block, act, ws, ws_n, None)
+
+
+def test_ffn_workspace_formula():
+    ws = A.lib().attn_ffn_workspace_bytes
+    assert ws(100, 256, 64) == 64 * 256 * 2                 # one block of 64 rows, bf16
+    assert ws(10, 256, 64) == 10 * 256 * 2                  # M < block: one block of M rows
+    assert ws(4096, 16384, 4096) == 4096 * 16384 * 2
+    assert ws(0, 256, 64) == 0 and ws(10, 0, 4) == 0 and ws(10, 256, 0) == 0
+
+
+def test_ffn_validation():
+    """Every rejection of attn_ffn_blockwise happens before any HIP call."""
+    assert ffn(x=None) == 1 and ffn(w1=None) == 1 and ffn(w2=None) == 1 and ffn(y=None) == 1
+    assert ffn(M=0) == 2 and ffn(block=0) == 2
+    assert ffn(d=48) == 3 and ffn(d_ff=100) == 3 and ffn(d=0) == 3     # multiples of 32
+    assert ffn(act=7) == 4
+    assert ffn(ws=None) == 6 and ffn(ws_n=64 * 256 * 2 - 1) == 6
+    assert ffn(x=ctypes.c_void_p(P[0].value + 8)) == 9 and ffn(y=ctypes.c_void_p(P[3].value + 2)) == 9
+    assert ffn(b1=ctypes.c_void_p(P[5].value + 2)) == 9 and ffn(ws=ctypes.c_void_p(P[4].value + 8)) == 9
+    assert ffn(y=ctypes.c_void_p(P[0].value + 64)) == 7      # Y overlaps X
+    assert ffn(ws=ctypes.c_void_p(P[1].value + 4096)) == 7   # workspace overlaps W1
+    assert ffn(y=P[4]) == 7                                   # Y overlaps the workspace
+    assert ffn(b2=ctypes.c_void_p(P[3].value + 16)) == 7     # Y overlaps b2
+    far = [ctypes.c_void_p((1 << 47) * (i + 1)) for i in range(6)]
+    # a hidden block of 2^31 bytes (65536 rows x 16384) and weights of 2^31 bytes (32768 x 32768) are refused
+    assert ffn(x=far[0], w1=far[1], w2=far[2], y=far[3], ws=far[4], M=65536, d=64, d_ff=16384, block=65536) == 2
+    assert ffn(x=far[0], w1=far[1], w2=far[2], y=far[3], ws=far[4], M=64, d=32768, d_ff=32768, block=64) == 2
+    assert "2^31" in last_error()
+
+
 def test_timing_read_without_launches():
     assert A.lib().attn_timing_enable(1) == 0
-    assert A.timing_read() == {"fwd": (0, 0.0), "merge": (0, 0.0), "copy": (0, 0.0)}
+    assert A.timing_read() == {"fwd": (0, 0.0), "merge": (0, 0.0), "copy": (0, 0.0), "ffn": (0, 0.0)}
     assert A.lib().attn_timing_enable(0) == 0
 
 

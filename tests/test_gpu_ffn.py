@@ -1,0 +1,100 @@
+"""GPU parity of the blockwise feed-forward (attn_ffn_blockwise, through the C ABI) against the fp64 oracle.
+
+Small shapes are compared in full: ragged row counts against the 256-row tiles and the block size, column
+counts that end in a partial 256-column tile, reduction lengths that are not multiples of 64, each
+activation, with and without biases.  The measured shape (the ring-share model's feed-forward) is
+compared on seeded rows that the oracle evaluates on their own.  Rows are independent, so the block size
+must not change a single bit of the result.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import exact_blockwise_attention_fwd_amd as A
+import oracle.ffn64 as F
+import workloads as W
+from parity import assert_parity, errors, out_to_f64, storage_to_f64, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    A.lib()
+
+
+def make(w: W.FfnWorkload):
+    st = [W.ffn_tensor(w, t) for t in (W.X_T, W.W1_T, W.B1_T, W.W2_T, W.B2_T)]
+    if not w.bias:
+        st[2] = st[4] = None
+    dev = [None if s is None else to_device(s) for s in st]
+    return st, dev
+
+
+def ffn_errors(y_dev, y_ref):
+    """errors() with the output in place of O and no LSE."""
+    y = out_to_f64(y_dev).reshape(y_ref.shape)
+    return errors(y, np.zeros(y.shape[0]), y_ref, np.zeros(y.shape[0]))
+
+
+SMALL = [
+    # M, d_model, d_ff, block, act, bias
+    (100, 64, 256, 64, "gelu", True),
+    (300, 128, 512, 128, "relu", True),
+    (1, 32, 32, 1, "gelu", True),
+    (257, 96, 320, 100, "gelu", False),
+    (513, 256, 1024, 512, "gelu", True),
+    (700, 160, 288, 700, "none", True),
+    (64, 512, 2048, 32, "relu", False),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "x".join(map(str, c[:4])) + f"-{c[4]}" + ("-b" if c[5] else ""))
+def test_ffn_small_vs_oracle(case):
+    M, d, d_ff, block, act, bias = case
+    w = W.FfnWorkload("ffn_small", M, d, d_ff, block, act, seed=5000 + M + d_ff, bias=bias)
+    st, (x, w1, b1, w2, b2) = make(w)
+    y = A.ffn_blockwise(x, w1, b1, w2, b2, block=block, act=act)
+    y_one = A.ffn_blockwise(x, w1, b1, w2, b2, block=M, act=act)
+    torch.cuda.synchronize()
+    ref = F.ffn_rows(storage_to_f64(st[0]), storage_to_f64(st[1]), st[2], storage_to_f64(st[3]), st[4], act)
+    err = ffn_errors(y, ref)
+    print(w, err, flush=True)
+    assert_parity(err, "bf16", f"ffn {case}")
+    assert torch.equal(y, y_one), "the block size changed the result"
+
+
+def test_ffn_output_buffer_and_workspace_reuse():
+    """A caller-supplied output and workspace, two calls of different sizes in a row, and NaN-poisoned output."""
+    outs = []
+    for M in (600, 250):
+        w = W.FfnWorkload("ffn_reuse", M, 128, 512, 200, "gelu", seed=5100)
+        st, (x, w1, b1, w2, b2) = make(w)
+        ws = torch.empty(A.ffn_workspace_bytes(600, 512, 200), dtype=torch.uint8, device="cuda")
+        y = torch.full((M, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+        r = A.ffn_blockwise(x, w1, b1, w2, b2, block=200, out=y, workspace=ws)
+        torch.cuda.synchronize()
+        assert r.data_ptr() == y.data_ptr()
+        ref = F.ffn_rows(storage_to_f64(st[0]), storage_to_f64(st[1]), st[2], storage_to_f64(st[3]), st[4], "gelu")
+        err = ffn_errors(y, ref)
+        assert not err["nan"]
+        assert_parity(err, "bf16", f"ffn reuse M={M}")
+        outs.append(y)
+
+
+def test_ffn_ring_share_sampled():
+    """The measured shape (16384 rows, d_model 4096, d_ff 16384, blocks of 4096, GELU) in the launch
+    configuration the bench times: 64 seeded rows against the oracle."""
+    w = W.FFN_WORKLOADS["ffn_ring_share"]
+    st, (x, w1, b1, w2, b2) = make(w)
+    y = A.ffn_blockwise(x, w1, b1, w2, b2, block=w.block, act=w.act)
+    torch.cuda.synchronize()
+    rows = W.ffn_sample_rows(w)
+    ref = F.ffn_rows(storage_to_f64(st[0][rows]), storage_to_f64(st[1]), st[2], storage_to_f64(st[3]), st[4], w.act)
+    err = ffn_errors(y.index_select(0, torch.from_numpy(rows).cuda()), ref)
+    print(w, err, flush=True)
+    assert_parity(err, "bf16", "ffn ring share sampled rows")

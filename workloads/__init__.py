@@ -22,6 +22,12 @@ depend on where Q, K and V come from, only on their values):
   ring_share_128k    B1 H32 N_q 16384, N_kv 131072 in 8 chunks, d128 bf16, bottom-right causal
                      (the last chunk is the diagonal one, the earlier ones are fully visible)
   ulysses_share_256k B1 H8  N 262144         d128 bf16 causal, oracle on 64 seeded rows per head
+
+Blockwise feed-forward inputs (``FfnWorkload``) follow the same scheme with one stream per tensor
+(SeedSequence(seed, spawn_key=(20 + tensor,)), tensor 0 = X, 1 = W1, 2 = b1, 3 = W2, 4 = b2): X ~ N(0, 1)
+and the weights ~ N(0, 1/fan_in) rounded to bf16, the biases 0.1 * N(0, 1) kept fp32.  The measured
+shape is the feed-forward of the ring-share model: the 16384 local rows of d_model = 32 heads x 128 = 4096,
+d_ff = 4 x d_model, GELU, in blocks of 4096 rows.
 """
 from __future__ import annotations
 
@@ -147,3 +153,54 @@ def sample_rows(w: Workload, b: int, h: int) -> np.ndarray:
     g = _stream(w.row_seed, 3, b, h)
     return np.sort(g.choice(w.N_q, size=n, replace=False))
 
+
+# ------------------------------------------------------------------------------ blockwise feed-forward
+X_T, W1_T, B1_T, W2_T, B2_T = 0, 1, 2, 3, 4
+
+
+@dataclasses.dataclass(frozen=True)
+class FfnWorkload:
+    name: str
+    M: int              # rows of the sequence
+    d_model: int
+    d_ff: int
+    block: int          # rows per block
+    act: str            # "gelu", "relu" or "none"
+    seed: int
+    bias: bool = True
+    sample_rows: int = 0  # >0: the oracle is checked on this many seeded rows
+
+    def flops(self) -> float:
+        """Algorithmic FLOPs: two products of 2 * M * d_model * d_ff each."""
+        return 4.0 * self.M * self.d_model * self.d_ff
+
+
+FFN_WORKLOADS = {
+    w.name: w
+    for w in [
+        FfnWorkload("ffn_ring_share", 16384, 4096, 16384, 4096, "gelu", seed=6, sample_rows=64),
+    ]
+}
+
+
+def ffn_tensor(w: FfnWorkload, tensor: int) -> np.ndarray:
+    """One tensor of a feed-forward workload: X, W1, W2 as uint16 bf16 patterns, b1, b2 as float32."""
+    shape = {X_T: (w.M, w.d_model), W1_T: (w.d_ff, w.d_model), B1_T: (w.d_ff,), W2_T: (w.d_model, w.d_ff),
+             B2_T: (w.d_model,)}[tensor]
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(w.seed, spawn_key=(20 + tensor,))))
+    x = g.standard_normal(shape, dtype=np.float32)
+    if tensor in (B1_T, B2_T):
+        return x * np.float32(0.1)
+    if tensor == W1_T:
+        x *= np.float32(1.0 / math.sqrt(w.d_model))
+    elif tensor == W2_T:
+        x *= np.float32(1.0 / math.sqrt(w.d_ff))
+    return f32_to_bf16_bits(x)
+
+
+def ffn_sample_rows(w: FfnWorkload) -> np.ndarray:
+    """Seeded row subset: distinct rows drawn uniformly from [0, M), sorted (all rows if not sampled)."""
+    if not w.sample_rows or w.sample_rows >= w.M:
+        return np.arange(w.M)
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(w.seed, spawn_key=(30,))))
+    return np.sort(g.choice(w.M, size=w.sample_rows, replace=False))
