@@ -565,8 +565,8 @@ int attn_ffn_blockwise(const void* X, const void* W1, const float* b1, const voi
     g_last_error.clear();
     if (!X || !W1 || !W2 || !Y) return fail(ATTN_ERR_NULL_PTR, "X, W1, W2 and Y must be non-NULL");
     if (M < 1 || block < 1) return fail(ATTN_ERR_BAD_SHAPE, "M and block must be >= 1 (got %lld, %lld)", M, block);
-    if (d_model < 32 || d_ff < 32 || d_model % 32 || d_ff % 32)
-        return fail(ATTN_ERR_UNSUPPORTED_D, "d_model and d_ff must be positive multiples of 32 (got %d, %d)",
+    if (d_model < 64 || d_ff < 64 || d_model % 64 || d_ff % 64)
+        return fail(ATTN_ERR_UNSUPPORTED_D, "d_model and d_ff must be positive multiples of 64 (got %d, %d)",
                     d_model, d_ff);
     if (act != ATTN_ACT_NONE && act != ATTN_ACT_RELU && act != ATTN_ACT_GELU)
         return fail(ATTN_ERR_BAD_DTYPE, "unknown activation %d", (int)act);
@@ -578,9 +578,8 @@ int attn_ffn_blockwise(const void* X, const void* W1, const float* b1, const voi
                     "below 2^31 bytes",
                     rows, d_model, rows, d_ff, d_ff, d_model);
     if (M > (1LL << 40) / d_model) return fail(ATTN_ERR_BAD_SHAPE, "M*d_model too large");
-    if (!aligned16(X) || !aligned16(W1) || !aligned16(W2) || !aligned16(Y) ||
-        ((uintptr_t)b1 & 3) || ((uintptr_t)b2 & 3))
-        return fail(ATTN_ERR_MISALIGNED, "X, W1, W2, Y need 16-byte alignment and b1, b2 4-byte alignment");
+    if (!aligned16(X) || !aligned16(W1) || !aligned16(W2) || !aligned16(Y) || !aligned16(b1) || !aligned16(b2))
+        return fail(ATTN_ERR_MISALIGNED, "X, W1, W2, Y, b1 and b2 need 16-byte alignment");
     const size_t need = attn_ffn_workspace_bytes(M, d_ff, block);
     if (!workspace || workspace_bytes < need)
         return fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);

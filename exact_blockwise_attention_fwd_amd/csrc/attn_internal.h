@@ -38,7 +38,8 @@ struct MergeArgs {
 };
 
 // One bf16 GEMM of the blockwise feed-forward: C[m][n] = act(sum_k A[m][k] B[n][k] + bias[n]) in bf16, fp32
-// accumulation; A [rows][k] and B [n][k] K-contiguous, C [rows][n]; k and n multiples of 32; bias fp32 or NULL.
+// accumulation; A [rows][k] and B [n][k] K-contiguous, C [rows][n]; k and n multiples of 64; bias fp32 (16-byte
+// aligned) or NULL.
 struct GemmArgs {
     const void* a;
     const void* b;

@@ -12,10 +12,12 @@
 //  * the tile is computed transposed (C^T = B A^T, v_mfma_f32_32x32x16_bf16 with A = B rows and B = A rows)
 //    so that every lane ends with one row m of C and 4-element runs of its columns, which are stored as
 //    8-byte bf16 groups;
-//  * K advances in tiles of 32: A and B tiles (256 rows x 64 bytes each) move HBM -> LDS with
-//    buffer_load_dwordx4 ... lds into a ring of 4 stages, two k-tiles ahead of the one being computed, one
-//    barrier per k-tile; rows past the end of A or B read as zeros (the buffer resource's bound);
-//  * LDS rows are XOR-swizzled in 16-byte units (chunk c of row r sits in slot c ^ ((r >> 2) & 3)) so that
+//  * K advances in tiles of 64: A and B tiles (256 rows x 128 bytes each) move HBM -> LDS with
+//    buffer_load_dwordx4 ... lds into two stages, the next k-tile loading while one is computed, one
+//    barrier per k-tile; rows past the end of A or B read as zeros (the buffer resource's bound).  The
+//    MFMAs of a k-tile's last 16-deep quarter are issued after the next barrier, under that tile's first
+//    LDS reads (measured against 32-deep k-tiles in a ring of four: +5 % and +15 % on the two GEMMs);
+//  * LDS rows are XOR-swizzled in 16-byte units (chunk c of row r sits in slot c ^ ((r >> 1) & 7)) so that
 //    the operand reads of each 16-lane group hit 16 distinct bank groups; the swizzle is applied through
 //    the global chunk each lane fetches;
 //  * workgroups are ordered in groups of 4 row tiles with the column tile varying slowest inside a group,
@@ -33,10 +35,10 @@ namespace attn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) char lds_char;
@@ -45,9 +47,9 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 constexpr int NXCD = 8;
 constexpr unsigned BUF_RSRC_WORD3 = 0x00020000u;   // raw buffer, 32-bit data format, bounds-checked
 
-constexpr int G_BM = 256, G_BN = 256, G_BK = 32;    // C tile and k-tile
+constexpr int G_BM = 256, G_BN = 256, G_BK = 64;    // C tile and k-tile
 constexpr int G_NW = 8, G_THREADS = 64 * G_NW;
-constexpr int G_STAGES = 4, G_LEAD = 2;             // LDS ring; k-tiles in flight ahead of the computed one
+constexpr int G_STAGES = 2, G_LEAD = 1;             // LDS ring; k-tiles in flight ahead of the computed one
 constexpr int G_ROW = 2 * G_BK;                     // 64 bytes per LDS row
 constexpr int G_TILE = G_BM * G_ROW;                // 16 KiB per operand tile
 constexpr int G_STAGE = 2 * G_TILE;                 // A tile then B tile
@@ -60,7 +62,7 @@ static_assert(G_SEGS % G_NW == 0 && G_STAGES > G_LEAD, "tiling");
 
 enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2 };
 
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
@@ -75,10 +77,26 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
     return __builtin_bit_cast(unsigned, p);
 }
 
+// erf(z) by Abramowitz and Stegun, Handbook of Mathematical Functions, formula 7.1.26: for z >= 0,
+// erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2) with t = 1 / (1 + p z), |error| <= 1.5e-7;
+// odd in z.  About a dozen instructions against the library erff's few dozen, and far below the bf16
+// rounding the hidden block receives next.
+__device__ __forceinline__ float erf_as(float z) {
+    const float a = fabsf(z);
+    const float t = __frcp_rn(__builtin_fmaf(0.3275911f, a, 1.f));
+    float poly = __builtin_fmaf(1.061405429f, t, -1.453152027f);
+    poly = __builtin_fmaf(poly, t, 1.421413741f);
+    poly = __builtin_fmaf(poly, t, -0.284496736f);
+    poly = __builtin_fmaf(poly, t, 0.254829592f);
+    poly *= t;
+    const float e = __builtin_amdgcn_exp2f(-a * a * 1.4426950408889634f);   // exp(-z^2)
+    return copysignf(__builtin_fmaf(-poly, e, 1.f), z);
+}
+
 template <int ACT>
 __device__ __forceinline__ float activate(float x) {
     if constexpr (ACT == ACT_RELU) return fmaxf(x, 0.f);
-    else if constexpr (ACT == ACT_GELU) return 0.5f * x * (1.f + erff(x * 0.70710678118654752f));
+    else if constexpr (ACT == ACT_GELU) return 0.5f * x * (1.f + erf_as(x * 0.70710678118654752f));
     else return x;
 }
 
@@ -105,8 +123,8 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_nt_kernel(GemmArgs g, int t
     const int K = g.k;
     const int nk = K / G_BK;
 
-    // ---- loads: this wave fills segments wave and wave + 8 of the A and the B tile of every k-tile.  Lane L
-    // writes LDS row 16*seg + L/4, slot L%4, which must hold chunk (L%4) ^ swz(row) of that row.
+    // ---- loads: this wave fills segments wave + 8j of the A and the B tile of every k-tile.  Lane L writes
+    // LDS row 8*seg + L/8, slot L%8, which must hold chunk (L%8) ^ swz(row) of that row.
     const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((const char*)g.a + (size_t)m0 * K * 2), (short)0, (g.rows - m0) * K * 2, BUF_RSRC_WORD3);
     const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
@@ -114,8 +132,8 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_nt_kernel(GemmArgs g, int t
     int voff[G_SEG_PER_WAVE];
 #pragma unroll
     for (int j = 0; j < G_SEG_PER_WAVE; ++j) {
-        const int row = 16 * (wave + G_NW * j) + lane / 4;
-        voff[j] = row * K * 2 + 16 * ((lane % 4) ^ swz(row));
+        const int row = 8 * (wave + G_NW * j) + lane / 8;
+        voff[j] = row * K * 2 + 16 * ((lane % 8) ^ swz(row));
     }
     auto issue = [&](int kt) {
         lds_char* st = lds + (kt % G_STAGES) * G_STAGE;
@@ -128,9 +146,10 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_nt_kernel(GemmArgs g, int t
         }
     };
 
-    // ---- operand reads: row col of a 32-row block, k-chunk 2*ks + h (8 bf16) of the k-tile
+    // ---- operand reads: row col of a 32-row block, k-chunk 2*ks + h (8 bf16) of the k-tile; slot
+    // (2*ks + h) ^ swz = (h ^ swz) ^ 2*ks, so quarter ks flips bits of the ks = 0 offset
     const int wm0 = 64 * (wave % 4), wn0 = 128 * (wave / 4);
-    int aro[2], bro[4];   // byte offsets within a stage's A / B tile, for ks = 0 (ks = 1 flips chunk bit 1)
+    int aro[2], bro[4];   // byte offsets within a stage's A / B tile, for ks = 0
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
         const int r = wm0 + 32 * mb + col;
@@ -148,31 +167,64 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_nt_kernel(GemmArgs g, int t
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = f32x16{};
 
-    for (int t = 0; t < G_LEAD && t < nk; ++t) issue(t);
-    for (int kt = 0; kt < nk; ++kt) {
-        // this wave's loads of k-tile kt have landed (the later ones may fly); after the barrier every
-        // wave's have, and every wave is done with the stage that k-tile kt + LEAD overwrites (last read
-        // in iteration kt + LEAD - STAGES < kt)
-        if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F70 | G_LOADS);
+    // Fragments of two 16-deep quarters of a k-tile, alternating.  The MFMAs of the last quarter of k-tile
+    // kt run after the barrier of k-tile kt + 1, while that tile's first fragments are read, so every
+    // barrier is followed by MFMA work that needs no new LDS data.
+    u32x4 af0[2], bf0[4], af1[2], bf1[4];
+    auto read = [&](const lds_char* st, int ks, u32x4 (&af)[2], u32x4 (&bf)[4]) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) af[mb] = *(const lds_u32x4*)(st + (aro[mb] ^ (32 * ks)));
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) bf[nb] = *(const lds_u32x4*)(st + (bro[nb] ^ (32 * ks)));
+    };
+    auto mma = [&](const u32x4 (&af)[2], const u32x4 (&bf)[4]) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+                acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, bf[nb]), __builtin_bit_cast(bf16x8, af[mb]), acc[nb][mb], 0, 0, 0);
+    };
+    // This wave's loads of k-tile kt have landed (the later ones may fly); after the barrier every wave's
+    // have, and every wave is done reading the stage that k-tile kt + LEAD overwrites (last read in
+    // iteration kt + LEAD - STAGES < kt).
+    auto land = [&](int kt) {
+        if (G_LEAD > 1 && kt + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F70 | ((G_LEAD - 1) * G_LOADS));
         else __builtin_amdgcn_s_waitcnt(0x0F70);
         lds_barrier();
         if (kt + G_LEAD < nk) issue(kt + G_LEAD);
+    };
+
+    for (int t = 0; t < G_LEAD && t < nk; ++t) issue(t);
+    land(0);
+    read(lds, 0, af0, bf0);
+    read(lds, 1, af1, bf1);
+    mma(af0, bf0);
+    read(lds, 2, af0, bf0);
+    mma(af1, bf1);
+    read(lds, 3, af1, bf1);
+    mma(af0, bf0);
+    for (int kt = 1; kt < nk; ++kt) {
+        land(kt);
         const lds_char* st = lds + (kt % G_STAGES) * G_STAGE;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            u32x4 af[2], bf[4];
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) af[mb] = *(const lds_u32x4*)(st + (aro[mb] ^ (32 * ks)));
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) bf[nb] = *(const lds_u32x4*)(st + (bro[nb] ^ (32 * ks)));
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
-                    acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, bf[nb]), __builtin_bit_cast(bf16x8, af[mb]), acc[nb][mb], 0, 0, 0);
-        }
+        read(st, 0, af0, bf0);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(af1, bf1);                     // last quarter of k-tile kt - 1
+        __builtin_amdgcn_sched_barrier(0);
+        read(st, 1, af1, bf1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(af0, bf0);
+        __builtin_amdgcn_sched_barrier(0);
+        read(st, 2, af0, bf0);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(af1, bf1);
+        __builtin_amdgcn_sched_barrier(0);
+        read(st, 3, af1, bf1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(af0, bf0);
+        __builtin_amdgcn_sched_barrier(0);
     }
+    mma(af1, bf1);
 
     // ---- epilogue: lane holds C[m][n] for m = m0 + wm0 + 32*mb + col and n = n0 + wn0 + 32*nb + 8*q + 4*h + r
     // (accumulator element 4*q + r); bias, activation, bf16, 8-byte stores of 4 consecutive columns
@@ -187,12 +239,10 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_nt_kernel(GemmArgs g, int t
             for (int q = 0; q < 4; ++q) {
                 const int n = n0 + wn0 + 32 * nb + 8 * q + 4 * h;
                 if (n >= g.n) continue;
+                const f32x4 b4 = g.bias ? *reinterpret_cast<const f32x4*>(g.bias + n) : f32x4{0.f, 0.f, 0.f, 0.f};
                 float v[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float b = g.bias ? g.bias[n + r] : 0.f;
-                    v[r] = activate<ACT>(acc[nb][mb][4 * q + r] + b);
-                }
+                for (int r = 0; r < 4; ++r) v[r] = activate<ACT>(acc[nb][mb][4 * q + r] + b4[r]);
                 *reinterpret_cast<u32x2*>(crow + n) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
             }
         }

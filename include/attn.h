@@ -184,8 +184,8 @@ int attn_fwd_streamed(const void* Q, const void* K_host, const void* V_host, voi
  *   linear layer); b1 [d_ff] and b2 [d_model] fp32, or NULL for none; Y [M, d_model] bf16.
  *   Each block is two bf16 GEMMs with fp32 accumulation on the matrix cores; the hidden block is rounded
  *   to bf16 between them (bias and activation applied in fp32 before the rounding).
- *   d_model and d_ff: positive multiples of 32.  A row block, its hidden block and each weight must stay
- *   below 2^31 bytes.  X, W1, W2, Y and the workspace: 16-byte aligned; b1, b2: 4-byte aligned.
+ *   d_model and d_ff: positive multiples of 64.  A row block, its hidden block and each weight must stay
+ *   below 2^31 bytes.  X, W1, W2, Y, b1, b2 and the workspace: 16-byte aligned.
  *   The workspace holds min(block, M) * d_ff bf16 values (attn_ffn_workspace_bytes); it is overwritten.
  *   Y must not overlap any input or the workspace.  Enqueued on hip_stream like every call here.
  */

@@ -220,11 +220,12 @@ def test_ffn_validation():
     """Every rejection of attn_ffn_blockwise happens before any HIP call."""
     assert ffn(x=None) == 1 and ffn(w1=None) == 1 and ffn(w2=None) == 1 and ffn(y=None) == 1
     assert ffn(M=0) == 2 and ffn(block=0) == 2
-    assert ffn(d=48) == 3 and ffn(d_ff=100) == 3 and ffn(d=0) == 3     # multiples of 32
+    assert ffn(d=48) == 3 and ffn(d_ff=100) == 3 and ffn(d=0) == 3     # multiples of 64
+    assert ffn(d=96) == 3 and ffn(d_ff=288) == 3 and ffn(d=32) == 3
     assert ffn(act=7) == 4
     assert ffn(ws=None) == 6 and ffn(ws_n=64 * 256 * 2 - 1) == 6
     assert ffn(x=ctypes.c_void_p(P[0].value + 8)) == 9 and ffn(y=ctypes.c_void_p(P[3].value + 2)) == 9
-    assert ffn(b1=ctypes.c_void_p(P[5].value + 2)) == 9 and ffn(ws=ctypes.c_void_p(P[4].value + 8)) == 9
+    assert ffn(b1=ctypes.c_void_p(P[5].value + 4)) == 9 and ffn(ws=ctypes.c_void_p(P[4].value + 8)) == 9
     assert ffn(y=ctypes.c_void_p(P[0].value + 64)) == 7      # Y overlaps X
     assert ffn(ws=ctypes.c_void_p(P[1].value + 4096)) == 7   # workspace overlaps W1
     assert ffn(y=P[4]) == 7                                   # Y overlaps the workspace

@@ -1,7 +1,7 @@
 """GPU parity of the blockwise feed-forward (attn_ffn_blockwise, through the C ABI) against the fp64 oracle.
 
 Small shapes are compared in full: ragged row counts against the 256-row tiles and the block size, column
-counts that end in a partial 256-column tile, reduction lengths that are not multiples of 64, each
+counts that end in a partial 256-column tile, reduction lengths of one or several 64-deep k-tiles, each
 activation, with and without biases.  The measured shape (the ring-share model's feed-forward) is
 compared on seeded rows that the oracle evaluates on their own.  Rows are independent, so the block size
 must not change a single bit of the result.
@@ -45,10 +45,10 @@ SMALL = [
     # M, d_model, d_ff, block, act, bias
     (100, 64, 256, 64, "gelu", True),
     (300, 128, 512, 128, "relu", True),
-    (1, 32, 32, 1, "gelu", True),
-    (257, 96, 320, 100, "gelu", False),
+    (1, 64, 64, 1, "gelu", True),
+    (257, 192, 320, 100, "gelu", False),
     (513, 256, 1024, 512, "gelu", True),
-    (700, 160, 288, 700, "none", True),
+    (700, 320, 448, 700, "none", True),
     (64, 512, 2048, 32, "relu", False),
 ]
 
