@@ -144,6 +144,92 @@ def time_streamed(w, q, k, v, steps: int, compute_ms: float):
             "overlap_efficiency": round(max(compute_ms, copy_ms) / ms, 4)}
 
 
+def time_ffn(reps: int, cpu_rows: int):
+    """The blockwise feed-forward (next to attention in a blockwise transformer block) at the ring-share
+    model's shape: attn_ffn_blockwise timed with the library's events (two GEMM launches per row block),
+    the same two products through torch's bf16 matmul (hipBLASLt) with torch's GELU and bias adds, for
+    context, and the fp64 oracle on `cpu_rows` seeded rows (all BLAS threads)."""
+    import time
+
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import exact_blockwise_attention_fwd_amd as A
+    import workloads as W
+
+    fw = W.FFN_WORKLOADS["ffn_ring_share"]
+    st = [W.ffn_tensor(fw, t) for t in (W.X_T, W.W1_T, W.B1_T, W.W2_T, W.B2_T)]
+
+    def dev(s):
+        if s.dtype == np.uint16:
+            return torch.from_numpy(s.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(s).cuda()
+
+    x, w1, b1, w2, b2 = (dev(s) for s in st)
+    ws = torch.empty(A.ffn_workspace_bytes(fw.M, fw.d_ff, fw.block), dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+
+    def run():
+        A.ffn_blockwise(x, w1, b1, w2, b2, block=fw.block, act=fw.act, out=y, workspace=ws)
+
+    def timed(f, n):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for _ in range(2):   # warmup, outside the library's timing
+        run()
+    torch.cuda.synchronize()
+    A.timing_enable(True)
+    A.timing_read()
+    ms = timed(run, reps)
+    A.timing_enable(False)
+    n_gemm, gemm_ms = A.timing_read()["ffn"]
+    w1t, w2t = w1.t().contiguous(), w2.t().contiguous()   # contiguous right operands for torch's products
+    y2 = torch.empty_like(x)
+
+    def vendor():
+        for r0 in range(0, fw.M, fw.block):
+            h = torch.nn.functional.gelu((x[r0:r0 + fw.block] @ w1t).float() + b1).to(torch.bfloat16)
+            y2[r0:r0 + fw.block] = ((h @ w2t).float() + b2).to(torch.bfloat16)
+
+    for _ in range(2):
+        vendor()
+    vms = timed(vendor, reps)
+    cpu = None
+    if cpu_rows > 0:   # the CPU-baseline leg: the oracle, timed as it stands
+        import oracle.ffn64 as F
+
+        rows = W.ffn_sample_rows(W.FfnWorkload(fw.name, fw.M, fw.d_model, fw.d_ff, fw.block, fw.act, fw.seed,
+                                               sample_rows=cpu_rows))
+        xr, w1r, w2r = (W.bf16_bits_to_f64(s) for s in (st[0][rows], st[1], st[3]))
+        t0 = time.perf_counter()
+        F.ffn_rows(xr, w1r, st[2], w2r, st[4], fw.act)
+        cpu_s = time.perf_counter() - t0
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        cpu = {"value": round(4.0 * len(rows) * fw.d_model * fw.d_ff / cpu_s / 1e12, 4), "unit": "TFLOP/s",
+               "cores": threads, "kind": "oracle",
+               "sample": f"fp64 oracle (oracle.ffn64.ffn_rows) on {len(rows)} seeded rows of the {fw.M}: {cpu_s:.1f} s"}
+    tflops = fw.flops() / (ms * 1e-3) / 1e12
+    return {"what": "attn_ffn_blockwise: act(x W1^T + b1) W2^T + b2 in blocks of rows",
+            "config": {"workload": fw.name, "M": fw.M, "d_model": fw.d_model, "d_ff": fw.d_ff, "block": fw.block,
+                       "act": fw.act},
+            "ms": round(ms, 4), "tflops": round(tflops, 2),
+            "gemm_launches": n_gemm / reps, "gemm_ms_avg": round(gemm_ms / max(n_gemm, 1), 4),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
+            "vendor_same_products": {"what": "torch bf16 matmul (hipBLASLt) for both products per block, torch GELU "
+                                             "and bias adds", "ms": round(vms, 4),
+                                     "tflops": round(fw.flops() / (vms * 1e-3) / 1e12, 2)},
+            "cpu_baseline": cpu}
+
+
 def cpu_baseline(w, seconds: float):
     """Time the fp64 oracle (blockwise form, key blocks of 1024, row blocks of 256) on a bounded sample of
     the workload: about `seconds` of wall time of (head, row block) pairs spread over the heads and over
@@ -263,6 +349,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-streamed", action="store_true", help="skip the host-streamed variant of the chunked step")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing of the step")
+    ap.add_argument("--no-ffn", action="store_true",
+                    help="skip the blockwise feed-forward leg (run with the ring-share workload only)")
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (practical HBM ceiling; also the "
@@ -379,6 +467,7 @@ def main():
         "counters": recorded_counters(w),
         "graph": None,
         "streamed": None,
+        "ffn": None,
         "cpu_baseline": None,
     }
     if w.dtype != "bf16":
@@ -394,6 +483,10 @@ def main():
         log("timing the host-streamed chunked step")
         out["streamed"] = time_streamed(w, q, k, v, max(2, min(args.steps, 5)), ms)
         log(f"streamed: {out['streamed']}")
+    if w.name == "ring_share_128k" and not args.no_ffn:
+        log("timing the blockwise feed-forward of the same model")
+        out["ffn"] = time_ffn(10, 0 if args.no_cpu_baseline else 4096)
+        log(f"ffn: {out['ffn']}")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

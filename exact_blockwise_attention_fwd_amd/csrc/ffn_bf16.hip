@@ -10,8 +10,8 @@
 //  * a workgroup computes a 256 x 256 tile of C with 8 waves (two per SIMD); wave w owns rows
 //    64*(w%4) .. +63 and columns 128*(w/4) .. +127, as 2 x 4 blocks of 32 x 32;
 //  * the tile is computed transposed (C^T = B A^T, v_mfma_f32_32x32x16_bf16 with A = B rows and B = A rows)
-//    so that every lane ends with one row m of C and 4-element runs of its columns, which are stored as
-//    8-byte bf16 groups;
+//    so that every lane ends with one row m of C and 4-element runs of its columns; the epilogue stages
+//    each wave's bf16 sub-tile in LDS and stores whole row segments;
 //  * K advances in tiles of 64: A and B tiles (256 rows x 128 bytes each) move HBM -> LDS with
 //    buffer_load_dwordx4 ... lds into two stages, the next k-tile loading while one is computed, one
 //    barrier per k-tile; rows past the end of A or B read as zeros (the buffer resource's bound).  The
@@ -43,6 +43,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 
 constexpr int NXCD = 8;
 constexpr unsigned BUF_RSRC_WORD3 = 0x00020000u;   // raw buffer, 32-bit data format, bounds-checked
@@ -226,26 +227,40 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_nt_kernel(GemmArgs g, int t
     }
     mma(af1, bf1);
 
-    // ---- epilogue: lane holds C[m][n] for m = m0 + wm0 + 32*mb + col and n = n0 + wn0 + 32*nb + 8*q + 4*h + r
-    // (accumulator element 4*q + r); bias, activation, bf16, 8-byte stores of 4 consecutive columns
+    // ---- epilogue: lane holds C[m][n] for tile row wm0 + 32*mb + col and tile column wn0 + 32*nb + 8*q + 4*h + r
+    // (accumulator element 4*q + r).  Bias and activation in fp32, bf16 into this wave's 16 KiB of LDS (its
+    // 64 x 128 sub-tile, 256 bytes per row, 16-byte unit u of row r kept at unit u ^ (r & 15) so that both
+    // the writes and the row reads are conflict-free), then whole 256-byte row segments to memory, four rows
+    // per store instruction (8-byte stores straight from the accumulators left partial lines that reached
+    // HBM twice over).
+    lds_barrier();   // every wave is done reading the operand stages
+    lds_char* const ct = lds + wave * 16384;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-        const int m = m0 + wm0 + 32 * mb + col;
-        if (m >= g.rows) continue;
-        uint16_t* crow = static_cast<uint16_t*>(g.c) + (size_t)m * g.n;
+        const int r = 32 * mb + col;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn0 + 32 * nb + 8 * q + 4 * h;
-                if (n >= g.n) continue;
-                const f32x4 b4 = g.bias ? *reinterpret_cast<const f32x4*>(g.bias + n) : f32x4{0.f, 0.f, 0.f, 0.f};
+                const int unit = 4 * nb + q;
+                const int n = n0 + wn0 + 8 * unit + 4 * h;
+                const f32x4 b4 = (g.bias && n < g.n) ? *reinterpret_cast<const f32x4*>(g.bias + n)
+                                                     : f32x4{0.f, 0.f, 0.f, 0.f};
                 float v[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = activate<ACT>(acc[nb][mb][4 * q + r] + b4[r]);
-                *reinterpret_cast<u32x2*>(crow + n) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+                for (int e = 0; e < 4; ++e) v[e] = activate<ACT>(acc[nb][mb][4 * q + e] + b4[e]);
+                *(lds_u32x2*)(ct + r * 256 + 16 * (unit ^ (r & 15)) + 8 * h) =
+                    u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
             }
         }
+    }
+    const int u = lane % 16;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = 4 * i + lane / 16;
+        const int m = m0 + wm0 + r, n = n0 + wn0 + 8 * u;
+        const u32x4 val = *(const lds_u32x4*)(ct + r * 256 + 16 * (u ^ (r & 15)));
+        if (m < g.rows && n < g.n) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.c) + (size_t)m * g.n + n) = val;
     }
 }
 
