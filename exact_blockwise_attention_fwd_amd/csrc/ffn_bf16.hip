@@ -8,7 +8,9 @@
 // The GEMM is C[m][n] = epi(sum_k A[m][k] B[n][k]) with both operands K-contiguous (activations row-major,
 // weights in the [out, in] layout), which is the layout the MFMA operands want:
 //  * a workgroup computes a 256 x 256 tile of C with 8 waves (two per SIMD); wave w owns rows
-//    64*(w%4) .. +63 and columns 128*(w/4) .. +127, as 2 x 4 blocks of 32 x 32;
+//    64*(w%4) .. +63 and columns 128*(w/4) .. +127, as 2 x 4 blocks of 32 x 32.  (FFN_GEMM_WAVES=4 builds
+//    the 4-wave form, 128 x 128 per wave: fewer LDS reads per MFMA, but with one wave per SIMD it measured
+//    about 10 % slower, and it needs the accumulators in AGPRs);
 //  * the tile is computed transposed (C^T = B A^T, v_mfma_f32_32x32x16_bf16 with A = B rows and B = A rows)
 //    so that every lane ends with one row m of C and 4-element runs of its columns; the epilogue stages
 //    each wave's bf16 sub-tile in LDS and stores whole row segments;
@@ -49,7 +51,12 @@ constexpr int NXCD = 8;
 constexpr unsigned BUF_RSRC_WORD3 = 0x00020000u;   // raw buffer, 32-bit data format, bounds-checked
 
 constexpr int G_BM = 256, G_BN = 256, G_BK = 64;    // C tile and k-tile
-constexpr int G_NW = 8, G_THREADS = 64 * G_NW;
+#ifndef FFN_GEMM_WAVES
+#define FFN_GEMM_WAVES 8
+#endif
+constexpr int G_NW = FFN_GEMM_WAVES, G_THREADS = 64 * G_NW;
+constexpr int G_WGM = G_NW == 8 ? 4 : 2;             // waves along the tile's rows (the rest along its columns)
+constexpr int G_MB = G_BM / G_WGM / 32, G_NB = G_BN / (G_NW / G_WGM) / 32;   // 32 x 32 blocks per wave
 constexpr int G_STAGES = 2, G_LEAD = 1;             // LDS ring; k-tiles in flight ahead of the computed one
 constexpr int G_ROW = 2 * G_BK;                     // 64 bytes per LDS row
 constexpr int G_TILE = G_BM * G_ROW;                // 16 KiB per operand tile
@@ -149,40 +156,40 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_nt_kernel(GemmArgs g, int t
 
     // ---- operand reads: row col of a 32-row block, k-chunk 2*ks + h (8 bf16) of the k-tile; slot
     // (2*ks + h) ^ swz = (h ^ swz) ^ 2*ks, so quarter ks flips bits of the ks = 0 offset
-    const int wm0 = 64 * (wave % 4), wn0 = 128 * (wave / 4);
-    int aro[2], bro[4];   // byte offsets within a stage's A / B tile, for ks = 0
+    const int wm0 = 32 * G_MB * (wave % G_WGM), wn0 = 32 * G_NB * (wave / G_WGM);
+    int aro[G_MB], bro[G_NB];   // byte offsets within a stage's A / B tile, for ks = 0
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < G_MB; ++mb) {
         const int r = wm0 + 32 * mb + col;
         aro[mb] = r * G_ROW + 16 * (h ^ swz(r));
     }
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
+    for (int nb = 0; nb < G_NB; ++nb) {
         const int r = wn0 + 32 * nb + col;
         bro[nb] = G_TILE + r * G_ROW + 16 * (h ^ swz(r));
     }
 
-    f32x16 acc[4][2];
+    f32x16 acc[G_NB][G_MB];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < G_NB; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = f32x16{};
+        for (int mb = 0; mb < G_MB; ++mb) acc[nb][mb] = f32x16{};
 
     // Fragments of two 16-deep quarters of a k-tile, alternating.  The MFMAs of the last quarter of k-tile
     // kt run after the barrier of k-tile kt + 1, while that tile's first fragments are read, so every
     // barrier is followed by MFMA work that needs no new LDS data.
-    u32x4 af0[2], bf0[4], af1[2], bf1[4];
-    auto read = [&](const lds_char* st, int ks, u32x4 (&af)[2], u32x4 (&bf)[4]) {
+    u32x4 af0[G_MB], bf0[G_NB], af1[G_MB], bf1[G_NB];
+    auto read = [&](const lds_char* st, int ks, u32x4 (&af)[G_MB], u32x4 (&bf)[G_NB]) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) af[mb] = *(const lds_u32x4*)(st + (aro[mb] ^ (32 * ks)));
+        for (int mb = 0; mb < G_MB; ++mb) af[mb] = *(const lds_u32x4*)(st + (aro[mb] ^ (32 * ks)));
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) bf[nb] = *(const lds_u32x4*)(st + (bro[nb] ^ (32 * ks)));
+        for (int nb = 0; nb < G_NB; ++nb) bf[nb] = *(const lds_u32x4*)(st + (bro[nb] ^ (32 * ks)));
     };
-    auto mma = [&](const u32x4 (&af)[2], const u32x4 (&bf)[4]) {
+    auto mma = [&](const u32x4 (&af)[G_MB], const u32x4 (&bf)[G_NB]) {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < G_NB; ++nb)
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < G_MB; ++mb)
                 acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8, bf[nb]), __builtin_bit_cast(bf16x8, af[mb]), acc[nb][mb], 0, 0, 0);
     };
@@ -228,18 +235,19 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_nt_kernel(GemmArgs g, int t
     mma(af1, bf1);
 
     // ---- epilogue: lane holds C[m][n] for tile row wm0 + 32*mb + col and tile column wn0 + 32*nb + 8*q + 4*h + r
-    // (accumulator element 4*q + r).  Bias and activation in fp32, bf16 into this wave's 16 KiB of LDS (its
-    // 64 x 128 sub-tile, 256 bytes per row, 16-byte unit u of row r kept at unit u ^ (r & 15) so that both
+    // (accumulator element 4*q + r).  Bias and activation in fp32, bf16 into this wave's part of LDS (its
+    // sub-tile, 128 columns = 256 bytes per row, 16-byte unit u of row r kept at unit u ^ (r & 15) so that both
     // the writes and the row reads are conflict-free), then whole 256-byte row segments to memory, four rows
     // per store instruction (8-byte stores straight from the accumulators left partial lines that reached
     // HBM twice over).
     lds_barrier();   // every wave is done reading the operand stages
-    lds_char* const ct = lds + wave * 16384;
+    static_assert(G_NB == 4 && G_NW * 32 * G_MB * 256 <= G_LDS, "epilogue staging: 256-byte rows, 16 units");
+    lds_char* const ct = lds + wave * (32 * G_MB * 256);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < G_MB; ++mb) {
         const int r = 32 * mb + col;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
+        for (int nb = 0; nb < G_NB; ++nb) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int unit = 4 * nb + q;
@@ -256,7 +264,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm_nt_kernel(GemmArgs g, int t
     }
     const int u = lane % 16;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8 * G_MB; ++i) {
         const int r = 4 * i + lane / 16;
         const int m = m0 + wm0 + r, n = n0 + wn0 + 8 * u;
         const u32x4 val = *(const lds_u32x4*)(ct + r * 256 + 16 * (u ^ (r & 15)));
