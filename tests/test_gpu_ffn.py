@@ -98,3 +98,51 @@ def test_ffn_ring_share_sampled():
     err = ffn_errors(y.index_select(0, torch.from_numpy(rows).cuda()), ref)
     print(w, err, flush=True)
     assert_parity(err, "bf16", "ffn ring share sampled rows")
+
+
+def test_ffn_graph_capture_and_replay():
+    """attn_ffn_blockwise allocates nothing and never synchronises: captured into a HIP graph (three row
+    blocks, six GEMM launches) it replays bit for bit equal to the eager call, with eager work between."""
+    w = W.FfnWorkload("ffn_graph", 600, 128, 512, 256, "gelu", seed=5200)
+    st, (x, w1, b1, w2, b2) = make(w)
+    ws = torch.empty(A.ffn_workspace_bytes(w.M, w.d_ff, w.block), dtype=torch.uint8, device="cuda")
+    y = torch.empty((w.M, w.d_model), dtype=torch.bfloat16, device="cuda")
+    A.ffn_blockwise(x, w1, b1, w2, b2, block=w.block, out=y, workspace=ws)   # eager; sets the LDS attribute
+    torch.cuda.synchronize()
+    eager = y.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            A.ffn_blockwise(x, w1, b1, w2, b2, block=w.block, out=y, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        y.fill_(float("nan"))
+        ws.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager), f"replay {rep} differs from the eager result"
+
+
+def test_ffn_binding_checks():
+    """The binding refuses tensors whose dtype, shape or device differ from what the call reads or writes."""
+    w = W.FfnWorkload("ffn_bind", 64, 128, 256, 64, "gelu", seed=5300)
+    _, (x, w1, b1, w2, b2) = make(w)
+    bad = [
+        lambda: A.ffn_blockwise(x.float(), w1, b1, w2, b2),
+        lambda: A.ffn_blockwise(x, w1[:128].contiguous(), b1, w2, b2),
+        lambda: A.ffn_blockwise(x, w1, b1[:100].contiguous(), w2, b2),
+        lambda: A.ffn_blockwise(x, w1, b1.to(torch.bfloat16), w2, b2),
+        lambda: A.ffn_blockwise(x, w1, b1, w2.t().contiguous(), b2),
+        lambda: A.ffn_blockwise(x, w1, b1, w2, b2, act="swish"),
+        lambda: A.ffn_blockwise(x, w1, b1, w2, b2, out=torch.empty((64, 128), device="cuda")),
+        lambda: A.ffn_blockwise(x, w1, b1, w2, b2, workspace=torch.empty(1 << 20, dtype=torch.uint8)),
+        lambda: A.ffn_blockwise(x, w1, b1, w2, b2, block=64, workspace=torch.empty(16, dtype=torch.uint8,
+                                                                                  device="cuda")),
+    ]
+    for i, call in enumerate(bad):
+        with pytest.raises((ValueError, TypeError, A.AttnError)):
+            call()
+            pytest.fail(f"case {i} accepted")
