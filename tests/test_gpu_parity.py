@@ -193,6 +193,22 @@ def test_f32_large_launch():
     check_sampled(w, st, o, lse, what="fp32 16 heads x 4096 rows")
 
 
+@pytest.mark.parametrize("case", [(7, 73, 40, 70, 128, "bf16"), (7, 73, 40, 70, 64, "bf16"), (5, 61, 33, 20, 48, "f32")],
+                         ids=lambda c: "x".join(map(str, c[:5])) + c[5])
+def test_many_heads(case):
+    """Hundreds of (b, h) pairs with short rows: the head indexing and the XCD-aware workgroup order at a
+    workgroup count that is not a multiple of 8, causal with N_q < N_kv, chunked as well."""
+    B, H, N_q, N_kv, d, dt = case
+    w = W.Workload("heads", B, H, N_q, N_kv, d, dt, True, 1, seed=3600 + d)
+    st, (q, k, v) = make(w)
+    o_ref, l_ref = oracle_full(st, w)
+    o, lse = A.fwd(q, k, v, causal=True, scale=w.scale)
+    oc, lc = A.fwd_chunked(q, k, v, 3, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    assert_parity(errors(out_to_f64(o), out_to_f64(lse), o_ref, l_ref), dt, f"{w}")
+    assert_parity(errors(out_to_f64(oc), out_to_f64(lc), o_ref, l_ref), dt, f"{w} 3 chunks")
+
+
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_unusual_scales(scale, dt):
