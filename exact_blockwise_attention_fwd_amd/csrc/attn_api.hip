@@ -151,6 +151,10 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// No array this library reads or writes may span 2^56 bytes (64 PiB, far past any device's memory); every byte
+// count below is first formed in 128-bit arithmetic and checked against that bound, so none of them wraps.
+constexpr __int128 kMaxBytes = (__int128)1 << 56;
+
 struct FwdCheck {
     size_t q_bytes, kv_bytes, o_bytes, lse_bytes;
     long long kv_stride;
@@ -192,6 +196,8 @@ int check_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, 
     if (stride < head)
         return fail(ATTN_ERR_BAD_SHAPE, "kv_head_stride %lld is smaller than N_kv*d = %lld", stride, head);
     const long long bh = (long long)B * H;
+    if ((__int128)bh * N_q * d * 4 >= kMaxBytes || ((__int128)(bh - 1) * stride + head) * 4 >= kMaxBytes)
+        return fail(ATTN_ERR_BAD_SHAPE, "Q, K, V or O would span 2^56 bytes or more");
     const size_t ei = esize((attn_dtype)in_dtype), eo = esize((attn_dtype)out_dtype);
     out->q_bytes = (size_t)(bh * N_q * d) * ei;
     out->kv_bytes = (size_t)((bh - 1) * stride + head) * ei;
@@ -386,6 +392,7 @@ int attn_merge(const void* O_a, const float* lse_a, const void* O_b, const float
 size_t attn_fwd_chunked_workspace_bytes(int B, int H, int N_q, int d, int P) {
     if (B < 1 || H < 1 || N_q < 1 || d < 1 || P < 1) return 0;
     if (P == 1) return 0;
+    if ((__int128)B * H * N_q * d * 4 >= kMaxBytes) return 0;
     const size_t rows = (size_t)B * H * N_q;
     return align256(rows * d * sizeof(float)) + align256(rows * sizeof(float));
 }
@@ -450,6 +457,7 @@ int attn_fwd_chunked(const void* Q, const void* K, const void* V, void* O, float
 
 size_t attn_fwd_streamed_workspace_bytes(int B, int H, int N_q, int N_kv, int d, int P, attn_dtype dtype) {
     if (B < 1 || H < 1 || N_q < 1 || N_kv < 1 || d < 1 || P < 1 || !valid_dtype(dtype)) return 0;
+    if ((__int128)B * H * N_q * d * 4 >= kMaxBytes || (__int128)B * H * N_kv * d * 4 >= kMaxBytes) return 0;
     const size_t rows = (size_t)B * H * N_q;
     const size_t cmax = ((size_t)N_kv + P - 1) / P;   // the longest chunk
     const size_t slot = (size_t)B * H * cmax * d * esize(dtype);
@@ -556,6 +564,7 @@ int attn_fwd_streamed(const void* Q, const void* K_host, const void* V_host, voi
 
 size_t attn_ffn_workspace_bytes(long long M, int d_ff, long long block) {
     if (M < 1 || d_ff < 1 || block < 1) return 0;
+    if ((__int128)(block < M ? block : M) * d_ff * 2 >= kMaxBytes) return 0;
     return align256((size_t)(block < M ? block : M) * d_ff * 2);
 }
 
@@ -570,14 +579,14 @@ int attn_ffn_blockwise(const void* X, const void* W1, const float* b1, const voi
                     d_model, d_ff);
     if (act != ATTN_ACT_NONE && act != ATTN_ACT_RELU && act != ATTN_ACT_GELU)
         return fail(ATTN_ERR_BAD_DTYPE, "unknown activation %d", (int)act);
-    const long long rows = block < M ? block : M;
+    if (M > (1LL << 40) / d_model) return fail(ATTN_ERR_BAD_SHAPE, "M*d_model too large");
+    const long long rows = block < M ? block : M;   // at most 2^34 after the bound on M
     const long long lim = 0x7fffffffLL;
     if (rows * d_ff * 2 > lim || rows * d_model * 2 > lim || (long long)d_ff * d_model * 2 > lim)
         return fail(ATTN_ERR_BAD_SHAPE,
                     "a row block (%lld x %d), its hidden block (%lld x %d) and each weight (%d x %d) must stay "
                     "below 2^31 bytes",
                     rows, d_model, rows, d_ff, d_ff, d_model);
-    if (M > (1LL << 40) / d_model) return fail(ATTN_ERR_BAD_SHAPE, "M*d_model too large");
     if (!aligned16(X) || !aligned16(W1) || !aligned16(W2) || !aligned16(Y) || !aligned16(b1) || !aligned16(b2))
         return fail(ATTN_ERR_MISALIGNED, "X, W1, W2, Y, b1 and b2 need 16-byte alignment");
     const size_t need = attn_ffn_workspace_bytes(M, d_ff, block);

@@ -49,7 +49,8 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
 typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL_PTR = 1,           /* a required pointer is NULL */
-    ATTN_ERR_BAD_SHAPE = 2,          /* B, H, N_q, N_kv, rows or P out of range, or a stride too small.
+    ATTN_ERR_BAD_SHAPE = 2,          /* B, H, N_q, N_kv, rows or P out of range, or a stride too small;
+                                        also any array that would span 2^56 bytes or more.
                                         Launch limits: ceil(N_q/128)*B*H (bf16) or ceil(N_q/64)*B*H (fp32)
                                         below 2^31-8; bf16 K of one head and launch below 2^31 bytes, i.e.
                                         N_kv <= 8,388,607 at d = 128 and 16,777,215 at d = 64 (in the
@@ -186,7 +187,8 @@ int attn_fwd_streamed(const void* Q, const void* K_host, const void* V_host, voi
  *   to bf16 between them (bias and activation applied in fp32 before the rounding).
  *   d_model and d_ff: positive multiples of 64.  A row block, its hidden block and each weight must stay
  *   below 2^31 bytes.  X, W1, W2, Y, b1, b2 and the workspace: 16-byte aligned.
- *   The workspace holds min(block, M) * d_ff bf16 values (attn_ffn_workspace_bytes); it is overwritten.
+ *   The workspace holds min(block, M) * d_ff bf16 values (attn_ffn_workspace_bytes, which returns 0 for
+ *   non-positive arguments); it is overwritten.
  *   Y must not overlap any input or the workspace.  Enqueued on hip_stream like every call here.
  */
 typedef enum { ATTN_ACT_NONE = 0, ATTN_ACT_RELU = 1, ATTN_ACT_GELU = 2 } attn_act;

@@ -143,6 +143,26 @@ def test_launch_limits():
     assert fwd(**kw, B=32768, H=1024, N_q=4096, N_kv=1, d=64, dtype=A.ATTN_F32) == 2
 
 
+def test_sizes_that_would_wrap():
+    """Shapes whose byte counts exceed 2^56 are refused (or give a zero workspace size) instead of wrapping
+    around 2^64 into a small size that a too-small workspace or an overlapping buffer would then pass."""
+    far = [ctypes.c_void_p((1 << 47) * (i + 1)) for i in range(8)]
+    kw = dict(q=far[0], k=far[1], v=far[2], o=far[3], lse=far[4])
+    assert fwd(**kw, B=1, H=1 << 30, N_q=1 << 30, N_kv=1, d=64) == 2
+    assert "2^56" in last_error()
+    assert fwd_ex(**kw, B=1, H=4, N_q=8, N_kv=8, d=64, stride=1 << 62) == 2   # K/V extent via the head stride
+    assert "2^56" in last_error()
+    lib = A.lib()
+    # B*H*N_q*d*4 = 2^70: the formula would wrap to 2^62; the size query reports it as invalid
+    assert lib.attn_fwd_chunked_workspace_bytes(1, 1 << 30, 1 << 30, 256, 2) == 0
+    assert lib.attn_fwd_chunked(far[0], far[1], far[2], far[3], far[4], 1, 1 << 30, 1 << 30, 8, 256, 0, 0.1, 2,
+                                A.ATTN_F32, far[5], 1 << 40, None) == 2
+    assert lib.attn_fwd_streamed_workspace_bytes(1, 1 << 30, 8, 1 << 30, 64, 2, A.ATTN_BF16) == 0
+    assert lib.attn_ffn_workspace_bytes(1 << 62, 16384, 1 << 62) == 0
+    assert ffn(x=far[0], w1=far[1], w2=far[2], y=far[3], ws=far[4], M=1 << 62, block=1 << 62) == 2
+    assert "too large" in last_error()
+
+
 def test_merge_validation():
     assert merge(oa=None) == 1
     assert merge(rows=0) == 2 and merge(d=0) == 2
