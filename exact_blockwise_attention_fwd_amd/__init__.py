@@ -92,6 +92,17 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+def _on(t):
+    """The library launches on the current HIP device: make it the tensors' device for the call."""
+    import torch
+    return torch.cuda.device(t.device)
+
+
+def _same_device(t, device, name):
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
 def _need(t, name):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
@@ -150,8 +161,9 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     out = _out(out, q.shape, dt, q.device, "out")
     lse = _out(lse, (B, H, N_q), ATTN_F32, q.device, "lse")
-    _check(lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                          B, H, N_q, N_kv, d, int(causal), scale, dt, _stream(q)), "attn_fwd")
+    with _on(q):
+        _check(lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                              B, H, N_q, N_kv, d, int(causal), scale, dt, _stream(q)), "attn_fwd")
     return out, lse
 
 
@@ -170,9 +182,10 @@ def fwd_ex(q, k, v, causal: bool = False, scale: float | None = None, causal_off
     out = _out(out, q.shape, odt, q.device, "out")
     lse = _out(lse, (B, H, N_q), ATTN_F32, q.device, "lse")
     es = q.element_size()
-    _check(lib().attn_fwd_ex(q.data_ptr(), k.data_ptr() + lo * d * es, v.data_ptr() + lo * d * es,
-                             out.data_ptr(), lse.data_ptr(), B, H, N_q, hi - lo, d, int(causal), scale,
-                             offset, n_total * d, dt, odt, _stream(q)), "attn_fwd_ex")
+    with _on(q):
+        _check(lib().attn_fwd_ex(q.data_ptr(), k.data_ptr() + lo * d * es, v.data_ptr() + lo * d * es,
+                                 out.data_ptr(), lse.data_ptr(), B, H, N_q, hi - lo, d, int(causal), scale,
+                                 offset, n_total * d, dt, odt, _stream(q)), "attn_fwd_ex")
     return out, lse
 
 
@@ -202,10 +215,11 @@ def fwd_acc(q, k, v, o_acc, lse_acc, causal: bool = False, scale: float | None =
     out = _out(out, q.shape, odt, q.device, "out")
     lse = _out(lse, (B, H, N_q), ATTN_F32, q.device, "lse")
     es = q.element_size()
-    _check(lib().attn_fwd_acc(q.data_ptr(), k.data_ptr() + lo * d * es, v.data_ptr() + lo * d * es,
-                              o_acc.data_ptr(), lse_acc.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N_q,
-                              hi - lo, d, int(causal), scale, offset, n_total * d, dt, odt, _stream(q)),
-           "attn_fwd_acc")
+    with _on(q):
+        _check(lib().attn_fwd_acc(q.data_ptr(), k.data_ptr() + lo * d * es, v.data_ptr() + lo * d * es,
+                                  o_acc.data_ptr(), lse_acc.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N_q,
+                                  hi - lo, d, int(causal), scale, offset, n_total * d, dt, odt, _stream(q)),
+               "attn_fwd_acc")
     return out, lse
 
 
@@ -232,8 +246,9 @@ def merge(o_a, lse_a, o_b, lse_b, out=None, lse=None, out_dtype=None):
     odt = _out_code(out, out_dtype, dt)
     out = _out(out, o_a.shape, odt, o_a.device, "out")
     lse = _out(lse, lse_a.shape, ATTN_F32, o_a.device, "lse")
-    _check(lib().attn_merge(o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(), lse_b.data_ptr(), out.data_ptr(),
-                            lse.data_ptr(), rows, d, dt, odt, _stream(o_a)), "attn_merge")
+    with _on(o_a):
+        _check(lib().attn_merge(o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(), lse_b.data_ptr(), out.data_ptr(),
+                                lse.data_ptr(), rows, d, dt, odt, _stream(o_a)), "attn_merge")
     return out, lse
 
 
@@ -256,11 +271,13 @@ def fwd_chunked(q, k, v, chunks: int, causal: bool = False, scale: float | None 
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     elif workspace is not None:
         _need(workspace, "workspace")
+        _same_device(workspace, q.device, "workspace")
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib().attn_fwd_chunked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                                  B, H, N_q, N_kv, d, int(causal), scale, int(chunks), dt, ws_ptr, ws_n,
-                                  _stream(q)), "attn_fwd_chunked")
+    with _on(q):
+        _check(lib().attn_fwd_chunked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                      B, H, N_q, N_kv, d, int(causal), scale, int(chunks), dt, ws_ptr, ws_n,
+                                      _stream(q)), "attn_fwd_chunked")
     return out, lse
 
 
@@ -295,12 +312,16 @@ def fwd_streamed(q, k_host, v_host, chunks: int, causal: bool = False, scale: fl
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace")
+    _same_device(workspace, q.device, "workspace")
     if copy_stream is None:
         copy_stream = torch.cuda.Stream(device=q.device)
-    _check(lib().attn_fwd_streamed(q.data_ptr(), k_host.data_ptr(), v_host.data_ptr(), out.data_ptr(),
-                                   lse.data_ptr(), B, H, N_q, N_kv, d, int(causal), scale, int(chunks), dt,
-                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q),
-                                   ctypes.c_void_p(copy_stream.cuda_stream)), "attn_fwd_streamed")
+    elif copy_stream.device != q.device:
+        raise ValueError(f"copy_stream must be on {q.device}, got {copy_stream.device}")
+    with _on(q):
+        _check(lib().attn_fwd_streamed(q.data_ptr(), k_host.data_ptr(), v_host.data_ptr(), out.data_ptr(),
+                                       lse.data_ptr(), B, H, N_q, N_kv, d, int(causal), scale, int(chunks), dt,
+                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q),
+                                       ctypes.c_void_p(copy_stream.cuda_stream)), "attn_fwd_streamed")
     return out, lse
 
 
@@ -342,10 +363,13 @@ def ffn_blockwise(x, w1, b1, w2, b2, block: int | None = None, act: str = "gelu"
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     _need(workspace, "workspace")
-    _check(lib().attn_ffn_blockwise(x.data_ptr(), w1.data_ptr(), None if b1 is None else b1.data_ptr(),
-                                    w2.data_ptr(), None if b2 is None else b2.data_ptr(), out.data_ptr(), M, d_model,
-                                    d_ff, block, ATTN_ACT[act], workspace.data_ptr(),
-                                    workspace.numel() * workspace.element_size(), _stream(x)), "attn_ffn_blockwise")
+    _same_device(workspace, x.device, "workspace")
+    with _on(x):
+        _check(lib().attn_ffn_blockwise(x.data_ptr(), w1.data_ptr(), None if b1 is None else b1.data_ptr(),
+                                        w2.data_ptr(), None if b2 is None else b2.data_ptr(), out.data_ptr(), M,
+                                        d_model, d_ff, block, ATTN_ACT[act], workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(), _stream(x)),
+               "attn_ffn_blockwise")
     return out
 
 

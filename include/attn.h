@@ -24,6 +24,9 @@
  *              1..256 for fp32.
  *   Ownership  the caller allocates and owns every buffer (device memory), including the chunked
  *              workspace; the library never allocates device memory and keeps no per-call state.
+ *   Device     every device buffer and stream of a call belongs to the calling thread's current HIP
+ *              device (hipSetDevice), where the kernels launch; the library keeps one set of launch
+ *              settings per device.
  *   Streams    every call enqueues on `hip_stream` (a hipStream_t; NULL = the null stream) and returns
  *              without synchronising.  Faults inside kernels surface at the caller's next synchronise.
  *              With the environment variable ATTN_DEBUG=1 every launch is followed by a synchronise and
