@@ -216,6 +216,29 @@ def test_streamed_validation():
     assert "workspace" in last_error() or "d = 64" in last_error()
 
 
+def test_last_error_is_per_thread():
+    """Two threads fail validation at the same time with different errors; each reads its own message
+    (ctypes drops the interpreter lock inside each call, so the calls interleave)."""
+    import threading
+    start = threading.Barrier(2)
+    bad = []
+
+    def worker(call, status, text):
+        start.wait()
+        for _ in range(2000):
+            if call() != status or text not in last_error():
+                bad.append((status, last_error()))
+                return
+
+    ts = [threading.Thread(target=worker, args=(lambda: fwd(scale=math.nan), 5, "finite")),
+          threading.Thread(target=worker, args=(lambda: fwd(d=48), 3, "d = 64 or 128"))]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not bad, bad
+
+
 def test_last_error_is_per_call():
     assert fwd(scale=math.nan) == 5
     assert "finite" in last_error()
