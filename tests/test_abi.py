@@ -216,6 +216,17 @@ def test_streamed_validation():
     assert "workspace" in last_error() or "d = 64" in last_error()
 
 
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one device's share: --gpus N > 1 exits with status 2 and says so, before it
+    touches a GPU."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=root)
+    assert r.returncode == 2 and "one GPU" in r.stderr and not r.stdout
+
+
 def test_last_error_is_per_thread():
     """Two threads fail validation at the same time with different errors; each reads its own message
     (ctypes drops the interpreter lock inside each call, so the calls interleave)."""
