@@ -146,3 +146,37 @@ def test_ffn_binding_checks():
         with pytest.raises((ValueError, TypeError, A.AttnError)):
             call()
             pytest.fail(f"case {i} accepted")
+
+
+@pytest.mark.parametrize("act,bias", [("relu", False), ("none", True)])
+def test_ffn_selection_weights_full_size_bit_exact(act, bias):
+    """Every output of the measured shape (16384 x 4096, d_ff 16384, blocks of 4096) checked bit for bit.  With
+    W1[n] the unit row e_sigma(n) and W2[j] the unit row e_tau(j) (sigma and tau seeded maps), each dot product
+    has exactly one non-zero term, so the exact result is known elementwise:
+        H[m][n] = act(X[m][sigma(n)] + b1[n])        rounded once to bf16 (the sum in fp32),
+        Y[m][j] = H[m][tau(j)] + b2[j]               rounded once to bf16 (the sum in fp32).
+    A misplaced tile, a skipped or repeated k-tile, a transposed operand or a wrong row block changes bits."""
+    M, d, d_ff, block = 16384, 4096, 16384, 4096
+    rng = np.random.default_rng(5400)
+    sigma = rng.integers(0, d, size=d_ff)
+    tau = rng.choice(d_ff, size=d, replace=False)
+    w = W.FfnWorkload("ffn_select", M, d, d_ff, block, act, seed=5401, bias=bias)
+    x_st = W.ffn_tensor(w, W.X_T)
+    one = W.f32_to_bf16_bits(np.ones(1, np.float32))[0]
+    w1 = np.zeros((d_ff, d), np.uint16)
+    w1[np.arange(d_ff), sigma] = one
+    w2 = np.zeros((d, d_ff), np.uint16)
+    w2[np.arange(d), tau] = one
+    b1 = W.ffn_tensor(w, W.B1_T) if bias else None
+    b2 = W.ffn_tensor(w, W.B2_T) if bias else None
+    x32 = W.bf16_bits_to_f64(x_st).astype(np.float32)
+    pre = x32[:, sigma[tau]] + (b1[tau] if bias else np.float32(0))      # fp32 sums, only the used columns
+    h = W.bf16_bits_to_f64(W.f32_to_bf16_bits(np.maximum(pre, 0) if act == "relu" else pre)).astype(np.float32)
+    want = W.f32_to_bf16_bits(h + (b2 if bias else np.float32(0)))
+    dev = [to_device(a) if a is not None else None for a in (x_st, w1, b1, w2, b2)]
+    y = A.ffn_blockwise(*dev, block=block, act=act)
+    torch.cuda.synchronize()
+    got = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    bad = int((got != want).sum())
+    print(f"act {act}, bias {bias}: {bad} of {got.size} outputs differ", flush=True)
+    assert bad == 0
