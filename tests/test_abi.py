@@ -216,6 +216,29 @@ def test_streamed_validation():
     assert "workspace" in last_error() or "d = 64" in last_error()
 
 
+def test_no_fallback_without_the_library(tmp_path):
+    """Without libattn.so every call that needs it raises ImportError, and host tensors are refused: there
+    is no CPU path to fall back to."""
+    import torch
+    saved = (A.LIB_PATH, A._lib)
+    try:
+        A.LIB_PATH, A._lib = str(tmp_path / "libattn.so"), None
+        with pytest.raises(ImportError):
+            A.lib()
+        with pytest.raises(ImportError):
+            A.workspace_bytes(1, 2, 8, 64, 4)
+        with pytest.raises(ImportError):
+            A.ffn_workspace_bytes(100, 256, 64)
+    finally:
+        A.LIB_PATH, A._lib = saved
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        A.fwd(q, q, q)
+    with pytest.raises(ValueError, match="device tensor"):
+        A.ffn_blockwise(torch.zeros(4, 64, dtype=torch.bfloat16), torch.zeros(64, 64, dtype=torch.bfloat16), None,
+                        torch.zeros(64, 64, dtype=torch.bfloat16), None)
+
+
 def test_bench_refuses_more_than_one_gpu():
     """bench.py measures one device's share: --gpus N > 1 exits with status 2 and says so, before it
     touches a GPU."""
