@@ -24,7 +24,8 @@
 //    the global chunk each lane fetches;
 //  * workgroups are ordered in groups of 4 row tiles with the column tile varying slowest inside a group,
 //    and each XCD takes a contiguous range of that order, so concurrently running tiles share A and B
-//    tiles in the XCD's L2.
+//    tiles in the XCD's L2 (groups of 8 speed up the 4096-column product by 3 % when it runs back to back,
+//    but not inside the feed-forward, where it follows the other product; 2 and 16 are slower).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
