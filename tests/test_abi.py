@@ -25,8 +25,9 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = A.lib()
     names = declared_functions()
-    assert {"attn_fwd", "attn_fwd_ex", "attn_fwd_acc", "attn_merge", "attn_fwd_chunked", "attn_fwd_chunked_workspace_bytes",
-            "attn_fwd_streamed", "attn_fwd_streamed_workspace_bytes", "attn_strerror", "attn_last_error",
+    assert {"attn_fwd", "attn_fwd_ex", "attn_fwd_acc", "attn_merge", "attn_fwd_chunked",
+            "attn_fwd_chunked_workspace_bytes", "attn_fwd_streamed", "attn_fwd_streamed_workspace_bytes",
+            "attn_strerror", "attn_last_error",
             "attn_ffn_blockwise", "attn_ffn_workspace_bytes", "attn_timing_enable", "attn_timing_read"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in attn.h but not exported"

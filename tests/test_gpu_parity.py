@@ -193,7 +193,8 @@ def test_f32_large_launch():
     check_sampled(w, st, o, lse, what="fp32 16 heads x 4096 rows")
 
 
-@pytest.mark.parametrize("case", [(7, 73, 40, 70, 128, "bf16"), (7, 73, 40, 70, 64, "bf16"), (5, 61, 33, 20, 48, "f32")],
+@pytest.mark.parametrize("case", [(7, 73, 40, 70, 128, "bf16"), (7, 73, 40, 70, 64, "bf16"),
+                                  (5, 61, 33, 20, 48, "f32")],
                          ids=lambda c: "x".join(map(str, c[:5])) + c[5])
 def test_many_heads(case):
     """Hundreds of (b, h) pairs with short rows: the head indexing and the XCD-aware workgroup order at a
@@ -255,6 +256,38 @@ def test_key_range_and_offset_partials():
     pa = oracle.attention(qq, kk[:, :, :cut], vv[:, :, :cut], w.scale, True, off)
     err = errors(out_to_f64(oa), out_to_f64(la), *pa)
     assert_parity(err, "bf16", "partial a")
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64)])
+def test_merge_grouping_does_not_matter(dt, d):
+    """Partials over five ragged key ranges (fp32, explicit causal offsets) combined with attn_merge in four
+    groupings: left fold, right fold, a balanced tree and a shuffled order.  The merge is associative and
+    commutative ("ATTENTION2D" explainer, section 2), so each equals the oracle's whole within tolerance,
+    the property the 2-D and ring schemes rely on when partials arrive in any order."""
+    w = W.Workload("groupings", 1, 2, 300, 1111, d, dt, True, 1, seed=2300 + d)
+    st, (q, k, v) = make(w)
+    o_ref, l_ref = oracle_full(st, w)
+    cuts = [0, 97, 410, 411, 800, w.N_kv]          # one range of a single key
+    off = w.N_kv - w.N_q
+    parts = [A.fwd_ex(q, k, v, True, w.scale, causal_offset=off - lo, key_range=(lo, hi), out_dtype=torch.float32)
+             for lo, hi in zip(cuts[:-1], cuts[1:])]
+    m = lambda a, b: A.merge(a[0], a[1], b[0], b[1])
+    left = parts[0]
+    for p_ in parts[1:]:
+        left = m(left, p_)
+    right = parts[-1]
+    for p_ in reversed(parts[:-1]):
+        right = m(p_, right)
+    tree = m(m(parts[0], parts[1]), m(parts[2], m(parts[3], parts[4])))
+    shuffled = m(m(parts[3], parts[0]), m(m(parts[4], parts[2]), parts[1]))
+    torch.cuda.synchronize()
+    results = {"left fold": left, "right fold": right, "tree": tree, "shuffled": shuffled}
+    for name, (o, lse) in results.items():
+        err = errors(out_to_f64(o), out_to_f64(lse), o_ref, l_ref)
+        print(f"{dt} d{d} {name}: {err}", flush=True)
+        assert_parity(err, "f32" if dt == "f32" else "bf16", f"merge grouping {name}")
+        if dt == "f32":   # fp32 partials from fp32 inputs: the groupings differ only in rounding
+            assert float((o - left[0]).abs().max()) <= 1e-6
 
 
 # ------------------------------------------------------------------------- fused fold of a key range (acc)
