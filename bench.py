@@ -299,8 +299,9 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_counters.txt")
 
 def recorded_fields(path, w):
     """The machine-readable `key: value` lines of a counter summary under profiles/, or None when it is
-    missing, covers another workload, or was taken on a different forward-kernel source."""
-    import hashlib
+    missing, covers another workload, or was taken on a different build of the forward kernel (its source
+    or its compile flags)."""
+    from exact_blockwise_attention_fwd_amd.build import fingerprint
 
     try:
         fields = {}
@@ -308,8 +309,8 @@ def recorded_fields(path, w):
             if ":" in line and not line.startswith((" ", "#", "|")):
                 key, val = line.split(":", 1)
                 fields[key.strip()] = val.strip()
-        sha = hashlib.sha256(open(FWD_SOURCE, "rb").read()).hexdigest()
-        if fields.get("kernel_source_sha256") != sha or fields.get("workload") != w.name:
+        if fields.get("kernel_build_sha256") != fingerprint(os.path.basename(FWD_SOURCE)) or \
+                fields.get("workload") != w.name:
             return None
         return fields
     except OSError:
