@@ -328,6 +328,34 @@ def check_row_positions(impl, seed=20):
             _close(part[1], full[1][rows], 1e-14, "row positions lse")
 
 
+def check_batched_front_end(impl, seed=21):
+    """The batched front end over [B=2, H=3] heads (each head drawn with its own scale of values, so a head
+    mix-up shows) against the pure-Python brute force of every head on its own, for both forms, one and
+    three chunks, causal with N_q < N_kv, N_q > N_kv and an explicit offset, and non-causal."""
+    rng = np.random.default_rng(seed)
+    B, H = 2, 3
+    for n, n_kv, causal, off in [(5, 8, True, None), (8, 5, True, None), (6, 7, True, 2), (4, 6, False, None)]:
+        d, dv = 3, 2
+        scale_h = np.arange(1, B * H + 1, dtype=np.float64).reshape(B, H, 1, 1)
+        q = rng.standard_normal((B, H, n, d))
+        k = rng.standard_normal((B, H, n_kv, d))
+        v = rng.standard_normal((B, H, n_kv, dv)) * scale_h + 10.0 * scale_h
+        eff = n_kv - n if off is None else off
+        ref_o = np.zeros((B, H, n, dv))
+        ref_l = np.zeros((B, H, n))
+        for b in range(B):
+            for h in range(H):
+                o_bh, l_bh = _brute(q[b, h].tolist(), k[b, h].tolist(), v[b, h].tolist(), 0.7, causal, eff)
+                ref_o[b, h], ref_l[b, h] = o_bh, l_bh
+        for form in ("naive", "blockwise"):
+            for chunks in (1, 3):
+                o, lse = impl.attention(q, k, v, 0.7, causal, off, form=form, block=2, chunks=chunks)
+                what = f"batched {form} chunks={chunks} n={n} n_kv={n_kv} causal={causal} offset={off}"
+                _close(o, ref_o, 1e-12, what + " O")
+                _close(lse, ref_l, 1e-12, what + " lse")
+
+
 ALL_CHECKS = [check_golden_attention, check_golden_merge, check_torch_sdpa, check_scipy_softmax,
               check_bruteforce, check_closed_forms, check_empty_rows, check_blockwise_vs_naive,
-              check_merge_algebra, check_chunked_every_p, check_permutation, check_row_positions]
+              check_merge_algebra, check_chunked_every_p, check_permutation, check_row_positions,
+              check_batched_front_end]

@@ -35,6 +35,12 @@ MUTANTS = {
     "merge_no_normalise": ("/ den[..., None]", "/ 1.0"),
     "chunk_offset_not_shifted": ("scale, causal, offset - lo, rows)", "scale, causal, offset, rows)"),
     "chunk_overlap": ("lo, hi = cb[p], cb[p + 1]", "lo, hi = cb[p], min(cb[p + 1] + 1, n_kv)"),
+    "batched_heads_reversed": ("kf = k.reshape(-1, k.shape[-2], k.shape[-1])",
+                               "kf = k.reshape(-1, k.shape[-2], k.shape[-1])[::-1]"),
+    "batched_chunked_offset_dropped": ("chunked_head(qf[i], kf[i], vf[i], scale, causal, offset, None",
+                                       "chunked_head(qf[i], kf[i], vf[i], scale, causal, None, None"),
+    "batched_values_of_head_zero": ("vf = v.reshape(-1, v.shape[-2], d)",
+                                   "vf = np.repeat(v.reshape(-1, v.shape[-2], d)[:1], qf.shape[0], axis=0)"),
     "chunk_bounds_drop_last_key": ("return [(p * n_kv) // chunks for p in range(chunks + 1)]",
                                    "return [(p * (n_kv - 1)) // chunks for p in range(chunks + 1)]"),
 }
