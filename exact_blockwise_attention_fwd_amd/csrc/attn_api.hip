@@ -38,6 +38,9 @@ bool debug_sync() {
 }
 
 // ---------------------------------------------------------------------------------------- launch timing
+// Kinds of timed work (the length of attn_timing_read's arrays): forward kernel, merge kernel, chunk copy,
+// feed-forward GEMM.
+constexpr int kTimingKinds = 4;
 struct Timed {
     int kind;
     hipEvent_t start, stop;
@@ -58,11 +61,12 @@ hipEvent_t take_event() {
     return e;
 }
 
-// Synchronisation events of attn_fwd_streamed, four per call (two "copied", two "done").  A set goes back to
-// the pool with the event that completes last; it is handed out again only once that event has completed,
-// so no pending wait or record of an earlier call can see it re-recorded.
+// Synchronisation events of attn_fwd_streamed, five per call (two "copied", two "done" and one "entry").  A
+// set goes back to the pool with the event that completes last; it is handed out again only once that event
+// has completed, so no pending wait or record of an earlier call can see it re-recorded.
+constexpr int kQuadEvents = 5;
 struct EventQuad {
-    hipEvent_t e[4];
+    hipEvent_t e[kQuadEvents];
     hipEvent_t last;
 };
 std::mutex g_quad_mu;
@@ -80,7 +84,7 @@ EventQuad* take_quad() {
         }
     }
     EventQuad* q = new EventQuad{};
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < kQuadEvents; ++k) {
         if (hipEventCreateWithFlags(&q->e[k], hipEventDisableTiming) != hipSuccess) {
             for (int j = 0; j < k; ++j) hipEventDestroy(q->e[j]);
             delete q;
@@ -504,22 +508,27 @@ int attn_fwd_streamed(const void* Q, const void* K_host, const void* V_host, voi
     char* kslot[2] = {slots, slots + 2 * slot};
     char* vslot[2] = {slots + slot, slots + 3 * slot};
 
-    // copied[b]: slot b holds its chunk; done[b]: the kernel reading slot b has finished
+    // copied[b]: slot b holds its chunk; done[b]: the kernel reading slot b has finished; entry: everything
+    // enqueued on the compute stream before this call (an earlier call's kernels may still read the staging
+    // slots, and memory handed back to the caller's allocator may still be in use there)
     EventQuad* ev = take_quad();
     if (!ev) return fail(ATTN_ERR_HIP, "attn_fwd_streamed: hipEventCreate failed");
     hipEvent_t* copied = ev->e;
     hipEvent_t* done = ev->e + 2;
+    hipEvent_t entry = ev->e[4];
     const size_t n = live.size();
     auto bounds = [&](size_t i, long long& lo, long long& hi) {
         lo = (long long)live[i] * N_kv / P;
         hi = (long long)(live[i] + 1) * N_kv / P;
     };
-    auto copy = [&](size_t i) -> int {   // chunk i into slot i % 2, once the kernel of chunk i-2 is done with it
+    // chunk i into slot i % 2: the first two once the compute stream's earlier work is done, later ones once
+    // the kernel of chunk i-2 is done with the slot
+    auto copy = [&](size_t i) -> int {
         const int b = (int)(i & 1);
         long long lo, hi;
         bounds(i, lo, hi);
         const size_t row = (size_t)(hi - lo) * d * es, pitch = (size_t)N_kv * d * es;
-        if (i >= 2 && hipStreamWaitEvent(cs, done[b], 0) != hipSuccess)
+        if (hipStreamWaitEvent(cs, i >= 2 ? done[b] : entry, 0) != hipSuccess)
             return fail(ATTN_ERR_HIP, "attn_fwd_streamed: hipStreamWaitEvent failed");
         return run(2, cs, "attn_fwd_streamed copy", [&] {
             hipError_t e = hipMemcpy2DAsync(kslot[b], row, static_cast<const char*>(K_host) + lo * d * es, pitch, row,
@@ -549,6 +558,10 @@ int attn_fwd_streamed(const void* Q, const void* K_host, const void* V_host, voi
         if (hipEventRecord(done[b], s) != hipSuccess) return fail(ATTN_ERR_HIP, "attn_fwd_streamed: hipEventRecord failed");
         return ATTN_OK;
     };
+    if (hipEventRecord(entry, s) != hipSuccess) {
+        give_quad(ev, nullptr);   // nothing waits on the set yet
+        return fail(ATTN_ERR_HIP, "attn_fwd_streamed: hipEventRecord failed");
+    }
     st = copy(0);
     if (!st && n > 1) st = copy(1);
     for (size_t i = 0; i < n && !st; ++i) {
@@ -627,7 +640,7 @@ int attn_timing_read(long long counts[4], double total_ms[4]) {
         std::lock_guard<std::mutex> g(g_timing_mu);
         recs.swap(g_timed);
     }
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < kTimingKinds; ++k) {
         counts[k] = 0;
         total_ms[k] = 0.0;
     }
@@ -636,7 +649,7 @@ int attn_timing_read(long long counts[4], double total_ms[4]) {
         float ms = 0.f;
         if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) {
             st = fail(ATTN_ERR_HIP, "attn_timing_read: event query failed");
-        } else if (r.kind >= 0 && r.kind < 4) {
+        } else if (r.kind >= 0 && r.kind < kTimingKinds) {
             counts[r.kind] += 1;
             total_ms[r.kind] += ms;
         }

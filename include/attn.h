@@ -162,7 +162,9 @@ size_t attn_fwd_streamed_workspace_bytes(int B, int H, int N_q, int N_kv, int d,
  * overlap the computation; pageable memory gives the same result, serialised).  The chunks, their order,
  * the skipped chunks and the kernels are those of attn_fwd_chunked with the same P, so O and LSE equal its
  * result bit for bit.  Every launch and copy is enqueued and the call returns without synchronising;
- * `hip_stream` waits for each chunk's copy, and when its work is done every copy is done.  The caller keeps
+ * the first copies wait for everything enqueued on `hip_stream` before the call (so back-to-back calls may
+ * share one workspace and one copy stream), `hip_stream` waits for each chunk's copy, and when its work is
+ * done every copy is done.  The caller keeps
  * K_host, V_host and the workspace alive until then.  The two streams must differ (NULL is the
  * default stream; a non-blocking copy stream keeps the copies independent of it).
  * Errors: those of attn_fwd_chunked (the workspace must not overlap Q, O or LSE), ATTN_ERR_BAD_ALIAS for equal

@@ -217,6 +217,17 @@ def test_streamed_validation():
     assert "workspace" in last_error() or "d = 64" in last_error()
 
 
+def test_timing_read_writes_exactly_four_entries():
+    """attn_timing_read fills arrays of 4 (one entry per kind of timed work) and nothing past them: sentinels
+    placed right after each array survive (works without a GPU: no launch has been recorded)."""
+    counts = (ctypes.c_longlong * 8)(*([7] * 8))
+    ms = (ctypes.c_double * 8)(*([7.5] * 8))
+    lib = A.lib()
+    assert lib.attn_timing_read(counts, ms) == 0
+    assert list(counts[:4]) == [0] * 4 and list(ms[:4]) == [0.0] * 4
+    assert list(counts[4:]) == [7] * 4 and list(ms[4:]) == [7.5] * 4
+
+
 def test_no_fallback_without_the_library(tmp_path):
     """Without libattn.so every call that needs it raises ImportError, and host tensors are refused: there
     is no CPU path to fall back to."""

@@ -71,6 +71,41 @@ def check_sampled(w, st, o_dev, lse_dev, heads=None, what=""):
     return err
 
 
+def oracle_every_row(w, st, rb: int = 256, kb: int = 1024):
+    """The oracle's result for every row of every head: its blockwise form (key blocks of ``kb``), over row
+    blocks of ``rb`` queries on a thread pool of this host's cores (one BLAS thread each).  A causal row block
+    is given only the keys up to its last visible one: key blocks past it are wholly masked for every row
+    of the block and leave the running max, denominator and output unchanged, so this is the same result."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    o = np.empty((w.B, w.H, w.N_q, st[2].shape[-1]))
+    lse = np.empty((w.B, w.H, w.N_q))
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(workers) as ex:
+        for b in range(w.B):
+            for h in range(w.H):
+                q, k, v = (storage_to_f64(s[b, h]) for s in st)
+
+                def job(r0):
+                    rows = np.arange(r0, min(r0 + rb, w.N_q))
+                    end = w.N_kv if not w.causal else max(0, min(w.N_kv, int(rows[-1]) + w.offset + 1))
+                    o[b, h, rows], lse[b, h, rows] = oracle.blockwise_head(q[rows], k[:end], v[:end], w.scale,
+                                                                           w.causal, w.offset, rows, kb)
+
+                list(ex.map(job, range(0, w.N_q, rb)))
+    return o, lse
+
+
+def check_every_row(w, o_ref, l_ref, o_dev, lse_dev, what=""):
+    err = errors(out_to_f64(o_dev), out_to_f64(lse_dev), o_ref, l_ref)
+    print(f"{what} {err}", flush=True)
+    assert_parity(err, w.dtype, what)
+    return err
+
+
 # ------------------------------------------------------------------------------ small shapes, full compare
 SMALL = [
     # B, H, N_q, N_kv, d, causal, dtype
@@ -364,6 +399,8 @@ def test_merge_vs_oracle(din, dout, d):
     tol = 2e-2 if dout == "bf16" else 1e-5
     assert not err["nan"] and err["lse_inf_match"]
     assert err["max_abs"] <= tol and err["lse_abs"] <= 1e-5, err
+    if dout == "bf16":   # the bf16 tolerance pair: rounding the merged rows to bf16 costs ~2^-9/sqrt(3) rel-RMS
+        assert err["rel_rms"] <= 5e-3, err
 
 
 @pytest.mark.parametrize("din,dout,d", [("f32", "f32", 128), ("bf16", "f32", 64)])
@@ -534,28 +571,30 @@ def test_tiny_fp32_full_and_4_chunks():
 
 
 def test_causal_prefill_4k():
+    """Every row of every head against the oracle's blockwise form, and seeded rows against its plain form."""
     w = W.WORKLOADS["causal_prefill_4k"]
     st, (q, k, v) = make(w)
     o, lse = A.fwd(q, k, v, causal=True, scale=w.scale)
     torch.cuda.synchronize()
     check_sampled(w, st, o, lse, what="causal_prefill_4k sampled")
-    # two heads in full
-    for b, h in [(0, 0), (3, 15)]:
-        sub = [s[b:b + 1, h:h + 1] for s in st]
-        o_ref, l_ref = oracle_full(sub, w)
-        err = errors(out_to_f64(o[b:b + 1, h:h + 1]), out_to_f64(lse[b:b + 1, h:h + 1]), o_ref, l_ref)
-        assert_parity(err, "bf16", f"causal_prefill_4k head ({b},{h}) full")
+    o_ref, l_ref = oracle_every_row(w, st)
+    check_every_row(w, o_ref, l_ref, o, lse, what="causal_prefill_4k every row")
 
 
 def test_peaky_16k():
+    """Every row of every head against the oracle's blockwise form, and seeded rows against its plain form."""
     w = W.WORKLOADS["peaky_16k"]
     st, (q, k, v) = make(w)
     o, lse = A.fwd(q, k, v, causal=False, scale=w.scale)
     torch.cuda.synchronize()
     check_sampled(w, st, o, lse, what="peaky_16k sampled")
+    o_ref, l_ref = oracle_every_row(w, st)
+    check_every_row(w, o_ref, l_ref, o, lse, what="peaky_16k every row")
 
 
 def test_ring_share_128k_chunked():
+    """The chunked step the bench times (8 chunks folded in the forward epilogues) and the single pass, each
+    compared on every row of every head against the oracle's single-pass blockwise result."""
     w = W.WORKLOADS["ring_share_128k"]
     st, (q, k, v) = make(w)
     o, lse = A.fwd_chunked(q, k, v, w.chunks, causal=True, scale=w.scale)
@@ -563,10 +602,9 @@ def test_ring_share_128k_chunked():
     check_sampled(w, st, o, lse, what="ring_share_128k 8 chunks sampled")
     o1, l1 = A.fwd(q, k, v, causal=True, scale=w.scale)
     torch.cuda.synchronize()
-    check_sampled(w, st, o1, l1, heads={(0, 0), (0, 31)}, what="ring_share_128k single pass sampled")
-    # chunked = single pass at any size (GPU against GPU)
-    assert (o.float() - o1.float()).abs().max().item() <= 2e-2
-    assert (lse - l1).abs().max().item() <= 1e-4
+    o_ref, l_ref = oracle_every_row(w, st)
+    check_every_row(w, o_ref, l_ref, o, lse, what="ring_share_128k 8 chunks every row")
+    check_every_row(w, o_ref, l_ref, o1, l1, what="ring_share_128k single pass every row")
 
 
 def test_max_keys_per_launch():
@@ -639,6 +677,31 @@ def test_streamed_pageable_and_repeated_calls():
     for i, (o, lse) in enumerate(outs):
         ref = (oc, lc) if i % 2 == 0 else (oc2, lc2)
         assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1]), f"call {i} differs from the chunked result"
+
+
+def test_streamed_back_to_back_shared_workspace():
+    """Two calls in a row with different host K/V, one explicit workspace and one non-blocking copy stream:
+    the second call's first copies wait for the first call's last kernels (which still read the staging
+    slots), so each result equals attn_fwd_chunked's bit for bit.  Many query rows against few keys make
+    every chunk's kernel longer than its copy, the case where an unordered copy would overwrite a slot in use."""
+    w1 = W.Workload("streamed_b2b_1", 1, 8, 65536, 4096, 128, "bf16", False, 1, seed=4300)
+    w2 = W.Workload("streamed_b2b_2", 1, 8, 65536, 4096, 128, "bf16", False, 1, seed=4301)
+    _, (q, k1, v1) = make(w1)
+    _, (_, k2, v2) = make(w2)
+    P = 8
+    oc1, lc1 = A.fwd_chunked(q, k1, v1, P, scale=w1.scale)
+    oc2, lc2 = A.fwd_chunked(q, k2, v2, P, scale=w1.scale)
+    k1h, v1h, k2h, v2h = (t.cpu().pin_memory() for t in (k1, v1, k2, v2))
+    ws = torch.empty(A.streamed_workspace_bytes(1, 8, 65536, 4096, 128, P, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    cs = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(2):
+        o1, l1 = A.fwd_streamed(q, k1h, v1h, P, scale=w1.scale, workspace=ws, copy_stream=cs)
+        o2, l2 = A.fwd_streamed(q, k2h, v2h, P, scale=w1.scale, workspace=ws, copy_stream=cs)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, oc1) and torch.equal(l1, lc1), "first call differs from the chunked result"
+        assert torch.equal(o2, oc2) and torch.equal(l2, lc2), "second call differs from the chunked result"
 
 
 def test_streamed_ring_share_full_size():
