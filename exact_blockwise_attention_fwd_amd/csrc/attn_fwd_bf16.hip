@@ -37,6 +37,13 @@
 //    then at most 2^64, the fp32 sums stay far from overflow, and the single final division by the
 //    denominator accumulated against the same reference gives the running-max result up to rounding.
 //    The common path therefore has no row max, no rescale factor and no rescale of the accumulators.
+//  * The P.V products accumulate the weights rounded to bf16 (up to 2^-8 relative each).  The d = 64 kernel
+//    keeps two denominators per row: the fp32 sum of the weights, for the LSE, and the fp32 sum of their
+//    bf16 roundings (one v_dot2c_f32_bf16 per pair), by which it divides O, so a row's output is a convex
+//    combination of V rows with weights proportional to exactly the accumulated values and a dominant
+//    weight's rounding cancels.  The d = 128 kernel divides O by the fp32 sum (no extra instruction per
+//    pair): its O then carries the dominant weights' rounding, at most 2^-8 of the largest |V| entry in
+//    a row dominated by one key, and averaging out over rows spread across many keys.
 //  * Workgroup ids are remapped so that consecutive logical tiles (same head, neighbouring query rows,
 //    hence the same K/V stream) land on the same XCD and share its L2; causal launches start with the
 //    longest query tiles.
@@ -124,6 +131,12 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// acc + a.lo + a.hi for two packed bf16 weights, summed in fp32 (one v_dot2c_f32_bf16 against (1, 1))
+__device__ __forceinline__ float add_bf16_pair(unsigned a, float acc) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), ones, acc, false);
+}
+
 // Workgroup barrier ordering LDS accesses only: this wave's LDS reads have returned (lgkmcnt(0)) before it
 // arrives.  Tile loads into LDS that are still in flight are not waited for here (a release fence would
 // wait for all of them); callers wait with an explicit vmcnt for exactly the loads that must have landed.
@@ -135,16 +148,17 @@ __device__ __forceinline__ void lds_barrier() {
     __asm__ volatile("" ::: "memory");
 }
 
-// One query row's result from a bf16 kernel: O = acc / l and lse = m*|scale| + ln(l), or (0, -inf) when the
-// row saw no key; when the launch accumulates, folded into the running partial with the two-term merge
+// One query row's result from a bf16 kernel: O = acc / lt and lse = m*|scale| + ln(l), or (0, -inf) when the
+// row saw no key (l is the fp32 sum of the weights, lt the fp32 sum of their bf16 roundings, which are what
+// acc accumulated); when the launch accumulates, folded into the running partial with the two-term merge
 // (M = max of the two lse, weights exp(lse - M) normalised to sum 1, lse = M + ln of their sum).  Lane h
 // of the row's half-wave pair holds head-dim elements 32*db + 8*g + 4*h + (0..3) of acc[db].
 template <int NDB, bool OUT_F32>
 __device__ __forceinline__ void store_row(const FwdArgs& a, int bh, int qi, int h, const f32x16 (&acc)[NDB],
-                                          float l_tot, float m, float scale_abs) {
+                                          float l_tot, float lt_tot, float m, float scale_abs) {
     constexpr int D = 32 * NDB;
     const float lb = l_tot > 0.f ? m * scale_abs + logf(l_tot) : -INFINITY;
-    float cb = l_tot > 0.f ? 1.f / l_tot : 0.f;   // factor on this launch's accumulator
+    float cb = l_tot > 0.f && lt_tot > 0.f ? 1.f / lt_tot : 0.f;   // factor on this launch's accumulator
     float ca = 0.f;                               // factor on the previous partial
     float lse = lb;
     const float* op = nullptr;
@@ -302,11 +316,14 @@ __global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int db = 0; db < T::NDB; ++db) acc[qb][db] = f32x16{};
-    float m[QB], l[QB];   // exponent reference (running max of raw dot products, may lag) and denominator
+    // exponent reference (running max of raw dot products, may lag), the denominator (fp32 sum of the
+    // weights, for lse) and the sum of the weights' bf16 roundings (the weights P.V accumulates, for O)
+    float m[QB], l[QB], lt[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         m[qb] = -INFINITY;
         l[qb] = 0.f;      // this half-wave's keys only; the halves are added at the end
+        lt[qb] = 0.f;
     }
     u32x4 p_cur[QB][T::NKB][2];   // bf16 weights of the previous tile, consumed by its P.V one step later
 
@@ -400,12 +417,13 @@ __global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd
                 }
             }
             u32x4 p_next[QB][T::NKB][2];
-            float rs[QB];
+            float rs[QB], rt[QB];
             // weights of tile t against reference m (m*c == mc; 0 stands in while no reference exists)
             auto weights = [&](const float (&mc)[QB]) {
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
                     rs[qb] = 0.f;
+                    rt[qb] = 0.f;
 #pragma unroll
                     for (int kb = 0; kb < T::NKB; ++kb) {
                         float e[16];
@@ -420,8 +438,10 @@ __global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd
 #pragma unroll
                         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                            for (int w = 0; w < 4; ++w)
+                            for (int w = 0; w < 4; ++w) {
                                 p_next[qb][kb][ks][w] = pack_bf16(e[8 * ks + 2 * w], e[8 * ks + 2 * w + 1]);
+                                rt[qb] = add_bf16_pair(p_next[qb][kb][ks][w], rt[qb]);
+                            }
                     }
                 }
             };
@@ -459,7 +479,10 @@ __global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd
                 weights(mc);
             }
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) l[qb] = __builtin_fmaf(l[qb], alpha[qb], rs[qb]);
+            for (int qb = 0; qb < QB; ++qb) {
+                l[qb] = __builtin_fmaf(l[qb], alpha[qb], rs[qb]);
+                lt[qb] = __builtin_fmaf(lt[qb], alpha[qb], rt[qb]);
+            }
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -520,7 +543,8 @@ __global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd
     for (int qb = 0; qb < QB; ++qb) {
         const int qi = qw0 + 32 * qb + col;
         const float l_tot = l[qb] + wave_xor32(l[qb]);
-        if (qi < a.n_q) store_row<T::NDB, OUT_F32>(a, bh, qi, h, acc[qb], l_tot, m[qb], scale_abs);
+        const float lt_tot = lt[qb] + wave_xor32(lt[qb]);
+        if (qi < a.n_q) store_row<T::NDB, OUT_F32>(a, bh, qi, h, acc[qb], l_tot, lt_tot, m[qb], scale_abs);
     }
 }
 
