@@ -7,6 +7,7 @@ streams.  If the library has not been built, every call raises (there is no fall
 
     o, lse = fwd(q, k, v, causal=True)                # q, k, v: [B, H, N, d] cuda tensors, bf16 or fp32
     o, lse = fwd_chunked(q, k, v, chunks=8, causal=True)
+    o, lse = fwd_chunked_noalloc(q, k, v, chunks=8, causal=True)  # partial in a fixed scratch, no allocation
     o, lse = merge(o_a, lse_a, o_b, lse_b)
     o, lse = fwd_acc(q, k, v, o_acc, lse_acc, causal_offset=..., key_range=(lo, hi))   # fold a key range in
     o, lse = fwd_streamed(q, k_host, v_host, chunks=8, causal=True)  # k, v in pinned host memory
@@ -49,6 +50,7 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_chunked_workspace_bytes.argtypes = [i, i, i, i, i]
     L.attn_fwd_chunked_workspace_bytes.restype = sz
     L.attn_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp]
+    L.attn_fwd_chunked_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
     L.attn_fwd_streamed_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     L.attn_fwd_streamed_workspace_bytes.restype = sz
     L.attn_fwd_streamed.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp, vp]
@@ -61,7 +63,8 @@ def lib() -> ctypes.CDLL:
     L.attn_last_error.restype = ctypes.c_char_p
     L.attn_timing_enable.argtypes = [i]
     L.attn_timing_read.argtypes = [ctypes.POINTER(ll), ctypes.POINTER(ctypes.c_double)]
-    for name in ("attn_fwd", "attn_fwd_ex", "attn_fwd_acc", "attn_merge", "attn_fwd_chunked", "attn_fwd_streamed",
+    for name in ("attn_fwd", "attn_fwd_ex", "attn_fwd_acc", "attn_merge", "attn_fwd_chunked",
+                 "attn_fwd_chunked_noalloc", "attn_fwd_streamed",
                  "attn_ffn_blockwise", "attn_timing_enable", "attn_timing_read"):
         getattr(L, name).restype = i
     _lib = L
@@ -278,6 +281,26 @@ def fwd_chunked(q, k, v, chunks: int, causal: bool = False, scale: float | None 
         _check(lib().attn_fwd_chunked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                       B, H, N_q, N_kv, d, int(causal), scale, int(chunks), dt, ws_ptr, ws_n,
                                       _stream(q)), "attn_fwd_chunked")
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # ATTN_NOALLOC_SCRATCH_BYTES of include/attn.h
+
+
+def fwd_chunked_noalloc(q, k, v, chunks: int, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """fwd_chunked with the running partial in the library's fixed per-device scratch instead of a workspace
+    (attn_fwd_chunked_noalloc): for callers that cannot allocate; with `out` and `lse` given, nothing is
+    allocated.  Calls that overlap in time on one device share that scratch and race."""
+    dt = _qkv(q, k, v)
+    B, H, N_q, d = q.shape
+    N_kv = k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = _out(out, q.shape, dt, q.device, "out")
+    lse = _out(lse, (B, H, N_q), ATTN_F32, q.device, "lse")
+    with _on(q):
+        _check(lib().attn_fwd_chunked_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                              lse.data_ptr(), B, H, N_q, N_kv, d, int(causal), scale, int(chunks), dt,
+                                              _stream(q)), "attn_fwd_chunked_noalloc")
     return out, lse
 
 

@@ -86,7 +86,7 @@ EventQuad* take_quad() {
     EventQuad* q = new EventQuad{};
     for (int k = 0; k < kQuadEvents; ++k) {
         if (hipEventCreateWithFlags(&q->e[k], hipEventDisableTiming) != hipSuccess) {
-            for (int j = 0; j < k; ++j) hipEventDestroy(q->e[j]);
+            for (int j = 0; j < k; ++j) (void)hipEventDestroy(q->e[j]);
             delete q;
             return nullptr;
         }
@@ -401,16 +401,25 @@ size_t attn_fwd_chunked_workspace_bytes(int B, int H, int N_q, int d, int P) {
     return align256(rows * d * sizeof(float)) + align256(rows * sizeof(float));
 }
 
-int attn_fwd_chunked(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q,
-                     int N_kv, int d, int causal, float scale, int P, attn_dtype dtype, void* workspace,
-                     size_t workspace_bytes, void* hip_stream) {
-    g_last_error.clear();
-    FwdCheck c;
-    int st = check_fwd(Q, K, V, O, LSE, B, H, N_q, N_kv, d, scale, 0, dtype, dtype, &c);
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the chunked mode that need no workspace; on success *c describes the arrays.
+int check_chunked(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q, int N_kv,
+                  int d, float scale, int P, attn_dtype dtype, FwdCheck* c) {
+    int st = check_fwd(Q, K, V, O, LSE, B, H, N_q, N_kv, d, scale, 0, dtype, dtype, c);
     if (st) return st;
     if (P < 1) return fail(ATTN_ERR_BAD_SHAPE, "P must be >= 1 (got %d)", P);
-    if ((st = check_launch_limits(B, H, N_q, ((long long)N_kv + P - 1) / P, d, dtype))) return st;
-    hipStream_t s = (hipStream_t)hip_stream;
+    return check_launch_limits(B, H, N_q, ((long long)N_kv + P - 1) / P, d, dtype);
+}
+
+// The chunked fold of attn_fwd_chunked after check_chunked, with a workspace of at least
+// attn_fwd_chunked_workspace_bytes (unused when P == 1).
+int run_chunked(const FwdCheck& c, const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                int N_q, int N_kv, int d, int causal, float scale, int P, attn_dtype dtype, void* workspace,
+                size_t workspace_bytes, hipStream_t s) {
+    int st = ATTN_OK;
     const long long offset = (long long)N_kv - N_q;
     if (P == 1)
         return launch_fwd(Q, K, V, O, LSE, B, H, N_q, N_kv, d, causal, scale, offset, c.kv_stride, dtype, dtype, s);
@@ -457,6 +466,80 @@ int attn_fwd_chunked(const void* Q, const void* K, const void* V, void* O, float
         if (st) return st;
     }
     return ATTN_OK;
+}
+
+// ------------------------------------------------------------- fixed scratch of attn_fwd_chunked_noalloc
+// The running fp32 partial of attn_fwd_chunked_noalloc lives in `scratch`, one copy per device, which the HIP
+// runtime allocates when this file's device code is loaded on that device and holds until the process ends.
+// In host code the name `scratch` is a host-side placeholder, not a device address: the device address is
+// looked up once per device with hipGetSymbolAddress (with that device current), kept in g_scratch_ptr, and
+// only that address is handed to kernels.  Nothing in the fold needs the array cleared: the first live
+// chunk writes every row of the partial before any later chunk reads it.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};   // per device; written once, under g_scratch_mu
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// This device's copy of `scratch` (the calling thread's current device), or nullptr with *err set.
+void* scratch_address(hipError_t* err) {
+    int dev = 0;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= 64) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess) return nullptr;
+        if (ptr == nullptr) {
+            *err = hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_chunked_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q,
+                             int N_kv, int d, int causal, float scale, int P, attn_dtype dtype, void* hip_stream) {
+    g_last_error.clear();
+    FwdCheck c;
+    if (int st = check_chunked(Q, K, V, O, LSE, B, H, N_q, N_kv, d, scale, P, dtype, &c)) return st;
+    const size_t need = attn_fwd_chunked_workspace_bytes(B, H, N_q, d, P);
+    if (need > ATTN_NOALLOC_SCRATCH_BYTES)
+        return fail(ATTN_ERR_WORKSPACE_TOO_SMALL,
+                    "attn_fwd_chunked_noalloc: the running partial needs %zu bytes, more than its fixed scratch of %zu "
+                    "bytes (B*H*N_q*(d+1)*4 must fit); use attn_fwd_chunked with a workspace",
+                    need, (size_t)ATTN_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (need > 0) {
+        hipError_t e = hipSuccess;
+        ws = scratch_address(&e);
+        if (!ws) return fail(ATTN_ERR_HIP, "attn_fwd_chunked_noalloc: hipGetSymbolAddress failed: %s", hipGetErrorString(e));
+    }
+    return run_chunked(c, Q, K, V, O, LSE, B, H, N_q, N_kv, d, causal, scale, P, dtype, ws,
+                       (size_t)ATTN_NOALLOC_SCRATCH_BYTES, (hipStream_t)hip_stream);
+}
+
+int attn_fwd_chunked(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N_q,
+                     int N_kv, int d, int causal, float scale, int P, attn_dtype dtype, void* workspace,
+                     size_t workspace_bytes, void* hip_stream) {
+    g_last_error.clear();
+    FwdCheck c;
+    if (int st = check_chunked(Q, K, V, O, LSE, B, H, N_q, N_kv, d, scale, P, dtype, &c)) return st;
+    return run_chunked(c, Q, K, V, O, LSE, B, H, N_q, N_kv, d, causal, scale, P, dtype, workspace, workspace_bytes,
+                       (hipStream_t)hip_stream);
 }
 
 size_t attn_fwd_streamed_workspace_bytes(int B, int H, int N_q, int N_kv, int d, int P, attn_dtype dtype) {

@@ -147,6 +147,24 @@ int attn_fwd_chunked(const void* Q, const void* K, const void* V, void* O, float
                      attn_dtype dtype, void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * attn_fwd_chunked_noalloc - attn_fwd_chunked without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid allocation.  The
+ * running fp32 partial lives in a fixed array of ATTN_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * device it runs on, from the first call on that device until the process ends; the call itself allocates
+ * nothing.  The arguments, chunks, kernels and result are those of attn_fwd_chunked (bit for bit), and
+ * attn_fwd_chunked_workspace_bytes(B, H, N_q, d, P) must not exceed ATTN_NOALLOC_SCRATCH_BYTES (B*H*N_q up
+ * to 130,055 at d = 128 and 258,111 at d = 64), else ATTN_ERR_WORKSPACE_TOO_SMALL before anything is
+ * enqueued.  All calls on one device share that array and it keeps the last call's contents: calls that
+ * overlap in time on one device (other streams, other threads) race, so the caller orders them (one stream,
+ * or events).  P == 1 does not touch it.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int attn_fwd_chunked_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                             int B, int H, int N_q, int N_kv, int d, int causal, float scale, int P,
+                             attn_dtype dtype, void* hip_stream);
+
+/*
  * attn_fwd_streamed_workspace_bytes - device workspace attn_fwd_streamed needs: the fp32 partial output
  * [B,H,N_q,d] and lse [B,H,N_q] of attn_fwd_chunked, plus two staging slots, each holding the K and the V
  * rows of one chunk for every (b, h) ([B*H, ceil(N_kv/P), d] in `dtype`); every piece 256-byte aligned.

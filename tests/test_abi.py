@@ -217,6 +217,34 @@ def test_streamed_validation():
     assert "workspace" in last_error() or "d = 64" in last_error()
 
 
+def test_chunked_noalloc_validation():
+    """The allocation-free chunked entry point validates like attn_fwd_chunked and refuses, before any HIP call,
+    a running partial larger than its fixed scratch (ATTN_NOALLOC_SCRATCH_BYTES = 64 MiB)."""
+    lib = A.lib()
+
+    far = [ctypes.c_void_p((1 << 44) * (i + 1)) for i in range(5)]   # 16 TiB apart: no overlaps
+
+    def call(B=1, H=2, N_q=8, N_kv=8, d=64, P_=4, q=far[0], o=far[3], lse=far[4]):
+        return lib.attn_fwd_chunked_noalloc(q, far[1], far[2], o, lse, B, H, N_q, N_kv, d, 0, 0.125, P_, A.ATTN_BF16,
+                                            None)
+
+    assert A.NOALLOC_SCRATCH_BYTES == 64 << 20
+    header = open(HEADER).read()
+    assert "#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in header
+    assert call(q=None) == 1
+    assert call(P_=0) == 2
+    assert call(d=100) == 3
+    # at d = 128, 130,055 rows fit in 64 MiB (rows * 129 * 4 bytes, 256-byte aligned pieces) and 130,056 do not
+    ws = lambda rows: lib.attn_fwd_chunked_workspace_bytes(1, 1, rows, 128, 2)
+    assert ws(130055) <= A.NOALLOC_SCRATCH_BYTES < ws(130056)
+    assert call(B=1, H=1, N_q=130056, N_kv=64, d=128, P_=2) == 6
+    assert "fixed scratch" in last_error()
+    # at d = 64 the limit is 258,111 rows
+    ws64 = lambda rows: lib.attn_fwd_chunked_workspace_bytes(1, 1, rows, 64, 3)
+    assert ws64(258111) <= A.NOALLOC_SCRATCH_BYTES < ws64(258112)
+    assert call(B=1, H=1, N_q=258112, N_kv=64, d=64, P_=3) == 6
+
+
 def test_timing_read_writes_exactly_four_entries():
     """attn_timing_read fills arrays of 4 (one entry per kind of timed work) and nothing past them: sentinels
     placed right after each array survive (works without a GPU: no launch has been recorded)."""
