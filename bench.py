@@ -15,8 +15,11 @@ forward launches), timed with HIP events that the library records on the stream 
 `merge` times attn_merge on its own, in place on fp32 partials of the workload's shape (the operation the
 chunked step fuses into its forward launches), against the HBM peak.  `streamed` runs the same chunked step
 with K and V in page-locked host memory (attn_fwd_streamed): host-to-device GB/s of the chunk copies and how
-much of the shorter of copies and computation the overlap hides.  `cpu_baseline` times the fp64 CPU
-oracle on a bounded sample of the same workload on this host's cores.
+much of the shorter of copies and computation the overlap hides.  `ulysses` times the other causal
+long-sequence workload (B1 H8, 262144 queries and keys, d128, one pass) the same way.  `cpu_baseline` times the
+fp64 CPU oracle on a bounded sample of the same workload on this host's cores (and, inside `ulysses`, on that
+workload's seeded rows).  `counters` and `roofline.traffic` are read from the rocprofv3 harness's summaries
+under profiles/ when they were taken on this same build; `counters_source` and `traffic_source` say so.
 """
 from __future__ import annotations
 
@@ -69,6 +72,57 @@ def time_graph(step, steps: int) -> float:
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def time_workload(w, steps: int, warmup: int) -> dict:
+    """A second workload's step (single pass or chunked, as configured) on seeded inputs resident in HBM: ms
+    per step with events on the current stream, and the forward launches' TFLOP/s from the library's events
+    against the dense bf16 peak."""
+    import numpy as np
+    import torch
+
+    import exact_blockwise_attention_fwd_amd as A
+    import workloads as W
+
+    def dev(t):
+        s_ = W.tensor_storage(w, t)
+        return torch.from_numpy(s_.view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v = dev(W.Q_T), dev(W.K_T), dev(W.V_T)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N_q), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, A.workspace_bytes(w.B, w.H, w.N_q, w.d, w.chunks)), dtype=torch.uint8, device="cuda")
+
+    def step():
+        if w.chunks > 1:
+            A.fwd_chunked(q, k, v, w.chunks, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=ws)
+        else:
+            A.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    A.timing_enable(True)
+    A.timing_read()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    A.timing_enable(False)
+    n_fwd, fwd_ms = A.timing_read()["fwd"]
+    ms = e0.elapsed_time(e1) / steps
+    tf = w.flops() / (ms * 1e-3) / 1e12
+    ktf = w.flops() * steps / (fwd_ms * 1e-3) / 1e12
+    del q, k, v, o, lse, ws
+    torch.cuda.empty_cache()
+    return {"config": {"workload": w.name, "B": w.B, "H": w.H, "N_q": w.N_q, "N_kv": w.N_kv, "d": w.d,
+                       "causal": w.causal, "chunks": w.chunks},
+            "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4), "tflops": round(tf, 2),
+            "pct_bf16_peak": round(100 * tf / BF16_PEAK_TFLOPS, 2),
+            "fwd_kernel": {"launches_per_step": n_fwd / steps, "tflops": round(ktf, 2),
+                           "frac": round(ktf / BF16_PEAK_TFLOPS, 4)}}
 
 
 def time_merge(w, reps: int):
@@ -144,11 +198,11 @@ def time_streamed(w, q, k, v, steps: int, compute_ms: float):
             "overlap_efficiency": round(max(compute_ms, copy_ms) / ms, 4)}
 
 
-def time_ffn(reps: int, cpu_rows: int):
+def time_ffn(reps: int, cpu_rows: int, vendor_context: bool):
     """The blockwise feed-forward (next to attention in a blockwise transformer block) at the ring-share
-    model's shape: attn_ffn_blockwise timed with the library's events (two GEMM launches per row block),
-    the same two products through torch's bf16 matmul (hipBLASLt) with torch's GELU and bias adds, for
-    context, and the fp64 oracle on `cpu_rows` seeded rows (all BLAS threads)."""
+    model's shape: attn_ffn_blockwise timed with the library's events (two GEMM launches per row block) and
+    the fp64 oracle on `cpu_rows` seeded rows (all BLAS threads).  With `vendor_context`, also the same two
+    products through torch's bf16 matmul with torch's GELU and bias adds: context only, not a target."""
     import time
 
     import numpy as np
@@ -191,17 +245,19 @@ def time_ffn(reps: int, cpu_rows: int):
     ms = timed(run, reps)
     A.timing_enable(False)
     n_gemm, gemm_ms = A.timing_read()["ffn"]
-    w1t, w2t = w1.t().contiguous(), w2.t().contiguous()   # contiguous right operands for torch's products
-    y2 = torch.empty_like(x)
+    vms = None
+    if vendor_context:
+        w1t, w2t = w1.t().contiguous(), w2.t().contiguous()   # contiguous right operands for torch's products
+        y2 = torch.empty_like(x)
 
-    def vendor():
-        for r0 in range(0, fw.M, fw.block):
-            h = torch.nn.functional.gelu((x[r0:r0 + fw.block] @ w1t).float() + b1).to(torch.bfloat16)
-            y2[r0:r0 + fw.block] = ((h @ w2t).float() + b2).to(torch.bfloat16)
+        def vendor():
+            for r0 in range(0, fw.M, fw.block):
+                h = torch.nn.functional.gelu((x[r0:r0 + fw.block] @ w1t).float() + b1).to(torch.bfloat16)
+                y2[r0:r0 + fw.block] = ((h @ w2t).float() + b2).to(torch.bfloat16)
 
-    for _ in range(2):
-        vendor()
-    vms = timed(vendor, reps)
+        for _ in range(2):
+            vendor()
+        vms = timed(vendor, reps)
     cpu = None
     if cpu_rows > 0:   # the CPU-baseline leg: the oracle, timed as it stands
         import oracle.ffn64 as F
@@ -224,10 +280,73 @@ def time_ffn(reps: int, cpu_rows: int):
             "gemm_launches": n_gemm / reps, "gemm_ms_avg": round(gemm_ms / max(n_gemm, 1), 4),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
-            "vendor_same_products": {"what": "torch bf16 matmul (hipBLASLt) for both products per block, torch GELU "
-                                             "and bias adds", "ms": round(vms, 4),
-                                     "tflops": round(fw.flops() / (vms * 1e-3) / 1e12, 2)},
+            "context_only_torch_matmul": None if vms is None else {
+                "what": "context only, not a target: torch bf16 matmul for both products per block, torch GELU and "
+                        "bias adds", "ms": round(vms, 4), "tflops": round(fw.flops() / (vms * 1e-3) / 1e12, 2)},
             "cpu_baseline": cpu}
+
+
+def cpu_workers() -> int:
+    """Oracle worker threads: the host's CPUs this process may run on, at most 16 (the host share that goes
+    with one GPU on the measurement machines)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def host_facts() -> dict:
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"affinity_cpus": len(os.sched_getaffinity(0)), "worker_threads": cpu_workers(), "cpu_model": model}
+
+
+def cpu_baseline_sampled_rows(w):
+    """The oracle (plain form, one pass over all keys) on the seeded query rows per head that the GPU tests
+    check for a workload with a row sample (the Ulysses head share: 64 per head), timed on this host; each
+    head's rows in one call, the heads on a thread pool with one BLAS thread per worker."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import workloads as W
+
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    rows = {bh: W.sample_rows(w, *bh) for bh in heads}
+    data = {}
+
+    def run(bh):
+        q, k, v = data[bh]
+        r = rows[bh]
+        oracle.naive_head(q[r], k, v, w.scale, w.causal, w.offset, r)
+
+    dt = 0.0
+    with threadpool_limits(limits=1, user_api="blas"):
+        # inputs of two heads at a time (K and V of one head are 256 MiB each in fp64); generation is untimed
+        for i in range(0, len(heads), 2):
+            part = heads[i:i + 2]
+            for bh in part:
+                data[bh] = tuple(W.head_f64(w, t, *bh) for t in (W.Q_T, W.K_T, W.V_T))
+            t0 = time.perf_counter()
+            with ThreadPoolExecutor(len(part)) as ex:
+                list(ex.map(run, part))
+            dt += time.perf_counter() - t0
+            for bh in part:
+                del data[bh]
+    n_rows = sum(len(r) for r in rows.values())
+    vis = sum(float((np.minimum(w.N_kv, r + w.offset + 1) if w.causal else np.full(len(r), w.N_kv)).sum())
+              for r in rows.values())
+    flops = 4.0 * w.d * vis
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "kind": "oracle", "threads": min(2, len(heads)),
+            "sample": f"fp64 oracle (plain form) on the {n_rows} seeded query rows ({w.sample_rows} per head) of "
+                      f"{w.name}, each against all of its visible keys of the {w.N_kv}: {flops:.3e} FLOP in {dt:.1f} s",
+            "full_workload_estimate_s": round(w.flops() / (flops / dt), 1),
+            "estimate_note": "row-scaled estimate of the whole workload at this rate (an estimate, not measured)"}
 
 
 def cpu_baseline(w, seconds: float):
@@ -243,7 +362,7 @@ def cpu_baseline(w, seconds: float):
     import oracle
     import workloads as W
 
-    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    workers = cpu_workers()
     rb = 256
     starts = list(range(0, w.N_q, rb))
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
@@ -283,7 +402,7 @@ def cpu_baseline(w, seconds: float):
     vis = np.minimum(w.N_kv, rows + w.offset + 1) if w.causal else np.full(len(rows), w.N_kv)
     flops = 4.0 * w.d * float(vis.sum())
     return {
-        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle", **host_facts(),
         "sample": f"fp64 blockwise oracle (single pass, key blocks of 1024) on {len(jobs)} blocks of {rb} query "
                   f"rows: {per_head} blocks spread over the {w.N_q} rows of each of {nheads} of the {len(heads)} "
                   f"heads, each row against all of its visible keys of the {w.N_kv}; {flops:.3e} FLOP in {dt:.1f} s",
@@ -315,6 +434,17 @@ def recorded_fields(path, w):
         return fields
     except OSError:
         return None
+
+
+def recorded_source(path, w):
+    """Where a recorded field comes from, for the bench line: the summary file and the build it was taken on."""
+    f = recorded_fields(path, w)
+    if f is None:
+        return None
+    return {"source": "recorded", "file": os.path.relpath(path, ROOT),
+            "kernel_build_sha256": f.get("kernel_build_sha256"),
+            "note": "measured by the rocprofv3 harness (python -m exact_blockwise_attention_fwd_amd.profile) on an "
+                    "earlier run of this same build, not in this run"}
 
 
 def recorded_traffic(w):
@@ -353,6 +483,10 @@ def main():
     ap.add_argument("--no-ffn", action="store_true",
                     help="skip the blockwise feed-forward leg (run with the ring-share workload only)")
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
+    ap.add_argument("--no-ulysses", action="store_true",
+                    help="skip the Ulysses head-share object (run with the ring-share workload only)")
+    ap.add_argument("--ffn-vendor-context", action="store_true",
+                    help="also time torch's matmul for the feed-forward's products (context only)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (practical HBM ceiling; also the "
                          "reference size for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -466,6 +600,9 @@ def main():
                      "frac": None if fwd_tflops is None else round(fwd_tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": recorded_traffic(w)},
         "counters": recorded_counters(w),
+        "counters_source": recorded_source(COUNTERS_FILE, w),
+        "traffic_source": recorded_source(TRAFFIC_FILE, w),
+        "ulysses": None,
         "graph": None,
         "streamed": None,
         "ffn": None,
@@ -486,11 +623,20 @@ def main():
         log(f"streamed: {out['streamed']}")
     if w.name == "ring_share_128k" and not args.no_ffn:
         log("timing the blockwise feed-forward of the same model")
-        out["ffn"] = time_ffn(10, 0 if args.no_cpu_baseline else 4096)
+        out["ffn"] = time_ffn(10, 0 if args.no_cpu_baseline else 4096, args.ffn_vendor_context)
         log(f"ffn: {out['ffn']}")
+    if w.name == "ring_share_128k" and not args.no_ulysses:
+        log("timing the Ulysses head share (the other causal long-sequence workload)")
+        del q, k, v, o, lse, ws
+        torch.cuda.empty_cache()
+        out["ulysses"] = time_workload(W.WORKLOADS["ulysses_share_256k"], 5, 1)
+        log(f"ulysses: {out['ulysses']}")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        if out["ulysses"] is not None:
+            log("timing the CPU oracle on the Ulysses share's seeded rows")
+            out["ulysses"]["cpu_baseline"] = cpu_baseline_sampled_rows(W.WORKLOADS["ulysses_share_256k"])
     print(json.dumps(out), flush=True)
 
 

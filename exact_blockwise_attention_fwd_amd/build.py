@@ -26,7 +26,7 @@ SOURCES = ["attn_api.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_merge.
 # MFMA results are allocated to ordinary VGPRs where possible (the softmax reads the score accumulators
 # with VALU instructions; accumulators parked in AGPRs would need a copy per element and tile).
 CODEGEN_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Werror",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
@@ -93,5 +93,52 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     return LIB
 
 
+def resource_usage(out_path: str | None = None) -> str:
+    """Registers, scratch (spill) bytes and occupancy of every kernel, from the compiler's kernel-resource-usage
+    remarks for the device code as built (same flags).  Returns the summary text; writes it to out_path."""
+    import re
+
+    cc = hipcc()
+    rows = []
+    for src in SOURCES:
+        cmd = [cc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), "--cuda-device-only", "-c", os.path.join(CSRC, src),
+               "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage"]
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}")
+        cur = None
+        for line in r.stdout.splitlines():
+            m = re.search(r"remark: (?:\s*)(Function Name|TotalSGPRs|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|"
+                          r"Occupancy \[waves/SIMD\]|SGPRs Spill|VGPRs Spill|LDS Size \[bytes/block\]): (\S+)", line)
+            if not m:
+                continue
+            key, val = m.group(1), m.group(2)
+            if key == "Function Name":
+                cur = {"src": src, "name": val}
+                rows.append(cur)
+            elif cur is not None:
+                cur[key] = val
+    hdr = ("kernel", "source", "VGPRs", "AGPRs", "SGPRs", "scratch B/lane", "VGPR spill", "SGPR spill", "waves/SIMD")
+    lines = ["# Kernel resource usage (compiler remarks, -Rpass-analysis=kernel-resource-usage)", "",
+             "Command: python -m exact_blockwise_attention_fwd_amd.build --resource-usage (hipcc --cuda-device-only",
+             "with the library's own flags: " + " ".join(CODEGEN_FLAGS) + "; per-source: " +
+             "; ".join(f"{k}: {' '.join(v)}" for k, v in SOURCE_FLAGS.items()) + ")", "",
+             "| " + " | ".join(hdr) + " |", "|" + "---|" * len(hdr)]
+    for r_ in rows:
+        lines.append(f"| `{r_['name']}` | {r_['src']} | {r_.get('VGPRs')} | {r_.get('AGPRs')} | {r_.get('TotalSGPRs')} | "
+                     f"{r_.get('ScratchSize [bytes/lane]')} | {r_.get('VGPRs Spill')} | {r_.get('SGPRs Spill')} | "
+                     f"{r_.get('Occupancy [waves/SIMD]')} |")
+    lines += ["", "fingerprints (sha256 of source and code-generation flags):", ""]
+    lines += [f"{src}: {fingerprint(src)}" for src in SOURCES]
+    text = "\n".join(lines) + "\n"
+    if out_path:
+        with open(out_path, "w") as f:
+            f.write(text)
+    return text
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--resource-usage" in sys.argv:
+        print(resource_usage(os.path.join(ROOT, "profiles", "kernel_resource_usage.txt")))
+    else:
+        print(build(verbose="-v" in sys.argv))
