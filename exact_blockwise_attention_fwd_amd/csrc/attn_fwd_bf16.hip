@@ -600,12 +600,21 @@ struct P3 {
     static constexpr int NKB = BC / 32, NDB = D / 32, NKS = D / 16, ROW = 2 * D, TILE = BC * ROW;
     static constexpr int SEGS = TILE / 1024, SEGS_PER_WAVE = SEGS / NW;
     static constexpr int RPS = 1024 / ROW, LPR = ROW / 16;
-    static constexpr int L = NW == 8 ? 3 : 1;        // steps of lead for every tile load
-    static constexpr int NK = L + 2, NV = L + 1;     // K and V buffers
-    static constexpr int LDS = (NK + NV) * TILE;
+    // K and V buffers: K_j is loaded NK-2 steps and V_j NV-1 steps before its first use
+    static constexpr int NK = NW == 8 ? 4 : 3, NV = NW == 8 ? 4 : 2;
+    static constexpr int EXTRA = NK + NV >= NW + 1 ? 0 : NW + 1 - NK - NV;   // staging-only buffers
+    static constexpr int LDS = (NK + NV + EXTRA) * TILE;
     static constexpr int WSTRIDE = NW * RPS * ROW;   // bytes between the load segments of one wave
+    // retire(t) needs K_{t+2} (issued by retire(t+2-NK)) and V_t (by retire(t+1-NV)) to have landed; loads
+    // are issued K then V per retire, and this many load instructions issued after the later of the two
+    // may still be in flight
+    static constexpr int DK = NK - 2, DV = NV - 1;
+    static constexpr int AFTER = (DK < DV ? 1 + 2 * (DK - 1) : 2 * (DV - 1)) * SEGS_PER_WAVE;
+    static constexpr int LEAD = NK > NV - 1 ? NK : NV - 1;   // all loads up to retire(t-1) exist iff t-1+LEAD < ntiles
     static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
-    static_assert(NK + NV >= NW + 1, "the epilogue stages every wave's rows in its own free K/V buffer");
+    static_assert(NK + NV + EXTRA >= NW + 1, "the epilogue stages every wave's rows in its own free buffer");
+    static_assert((NK - 1) * TILE + 32 * ROW < 65536 && (NV - 1) * TILE + 52 * ROW < 65536,
+                  "constant buffer bases fit the LDS reads' 16-bit offset field");
 };
 
 template <int NW, bool CAUSAL, bool OUT_F32>
@@ -676,13 +685,20 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
     };
     // Buffer bases pass through an empty statement as scalars, so that the compiler cannot split a constant
     // out of them into every read's address (it would be negative, which the offset field cannot hold).
+    // An LDS address as a plain number: this kernel declares no static LDS, so its dynamic LDS starts at
+    // address 0.  A constant built this way folds into the reads' offset fields; one built from the
+    // dynamic-LDS symbol keeps an add of its (zero) base per per-lane offset.
+    auto lds_at = [](int byte) __attribute__((always_inline)) { return (const lds_char*)(uintptr_t)byte; };
     auto kbuf_of = [&](int j) __attribute__((always_inline)) {
         int o = (j % T::NK) * T::TILE;
         __asm__ volatile("" : "+s"(o));
         return (const lds_char*)(lds + o);
     };
+    // V buffer j: relative to the V region in the eight-wave kernel (its V offsets carry the region's base, so
+    // that constant buffer bases fit the reads' offset fields), absolute in the four-wave one
+    constexpr int VBASE = T::NW == 8 ? T::NK * T::TILE : 0;
     auto vbuf_of = [&](int j) __attribute__((always_inline)) {
-        int o = (T::NK + (j % T::NV)) * T::TILE;
+        int o = (T::NK - VBASE / T::TILE + (j % T::NV)) * T::TILE;
         __asm__ volatile("" : "+s"(o));
         return (const lds_char*)(lds + o);
     };
@@ -714,7 +730,7 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
 #pragma unroll
         for (int db = 0; db < T::NDB; ++db) {
             const int chunk = 4 * db + 2 * dp + (s4 >> 1);
-            v_roff[db] = (8 * h + e) * T::ROW + 16 * (chunk ^ v_swz<D>(e)) + 8 * (s4 & 1);
+            v_roff[db] = VBASE + (8 * h + e) * T::ROW + 16 * (chunk ^ v_swz<D>(e)) + 8 * (s4 & 1);
         }
     }
 
@@ -896,7 +912,7 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
     auto retire = [&](int t) __attribute__((always_inline)) {
         // K_{t+2} and V_t were issued L steps ago; the loads of the L-1 later retires may still fly (when
         // all of them exist; near the end, wait for everything)
-        if (t + T::L + 1 < ntiles) __builtin_amdgcn_s_waitcnt(0x0F70 | ((T::L - 1) * 2 * T::SEGS_PER_WAVE));
+        if (t - 1 + T::LEAD < ntiles) __builtin_amdgcn_s_waitcnt(0x0F70 | T::AFTER);
         else __builtin_amdgcn_s_waitcnt(0x0F70);
         lds_barrier();
         load_k(t + T::NK);
@@ -938,7 +954,22 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
         if (nt > 1) {
             step(yes{}, no{}, yes{}, 0, kbuf_of(1), kbuf_of(0), vbuf_of(0));
             retire(0);
-            for (t = 1; t < nt - 1; ++t) {
+            // middle steps, four at a time with every buffer base a constant (t = 1 mod 4 at the start of
+            // each group: K_{t+1}, K_t and V_{t-1} sit in buffers 2, 1 and 0, then 3, 2, 1, ...)
+            static_assert((T::NK == 4 && T::NV == 4) || T::NW != 8, "the unrolled steps assume four K and four V buffers");
+            t = 1;
+            if constexpr (T::NW == 8) {
+                for (; t + 4 < nt; t += 4) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int ph = (1 + u) & 3;   // t + u mod 4
+                        step(yes{}, yes{}, yes{}, t + u, lds_at(((ph + 1) & 3) * T::TILE), lds_at(ph * T::TILE),
+                             lds_at(((ph + 3) & 3) * T::TILE));
+                        retire(t + u);
+                    }
+                }
+            }
+            for (; t < nt - 1; ++t) {
                 step(yes{}, yes{}, yes{}, t, kbuf_of(t + 1), kbuf_of(t), vbuf_of(t - 1));
                 retire(t);
             }
@@ -963,6 +994,11 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
     // sum 1, lse = M + ln of their sum).  Lane (col, h) holds head-dim elements 32*db + 8*g + 4*h + (0..3)
     // of its row; the scaled rows go through LDS so that loads and stores cover whole rows.
     {
+        // The lane id passes through an empty statement here, so that the epilogue's per-lane addresses are
+        // formed after the key loop instead of being hoisted above it and kept (in private memory) across it.
+        int lane = tid & 63;
+        __asm__ volatile("" : "+v"(lane));
+        const int col = lane & 31;
         const int qi = qw0 + col;
         const float l_tot = l + wave_xor32(l);
         const float lb = l_tot > 0.f ? m * scale_abs + logf(l_tot) : -INFINITY;
