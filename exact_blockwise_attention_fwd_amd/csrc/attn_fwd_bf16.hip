@@ -759,12 +759,19 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
         const int kt = t * T::BC;
         const int qi = qw0 + col;
         const int lim = CAUSAL ? min(a.n_kv - 1, qi + a.offset) : a.n_kv - 1;
+        // slot j of key block kb holds key kt + 8h + (32 kb + 16 (j >> 3) + (j & 7)): one per-lane threshold
+        // against compile-time slot offsets, so no per-slot key index is kept in a register
+        const int thr = lim - kt - 8 * h;
 #pragma unroll
         for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const int key = kt + 32 * kb + 16 * (j >> 3) + 8 * h + (j & 7);
-                if (key > lim) sc[kb][j] = -INFINITY;
+                // all ones where the key is past the limit; the element goes through a local first, since
+                // this compiler's __builtin_bit_cast of a vector-element operand reads element 0
+                const unsigned msk = (unsigned)((thr - (32 * kb + 16 * (j >> 3) + (j & 7))) >> 31);
+                const float x = sc[kb][j];
+                const unsigned b = __builtin_bit_cast(unsigned, x);
+                sc[kb][j] = __builtin_bit_cast(float, (b & ~msk) | (0xff800000u & msk));
             }
     };
     // weights and their row sum against reference mc (the plain form, used by the rare redo)
@@ -951,8 +958,11 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
     };
     if (nt > 0) {
         s_all(s, kbuf_of(0));
+        // Step 0: the softmax of tile 0 and S(1).  A wave with a single tile runs the same step (one call site
+        // for both cases, so no second copy of the read offsets is kept across the loop) with its S part
+        // recomputing the scores of tile 0, which nothing reads: its weights are already packed for P.V.
+        step(yes{}, no{}, yes{}, 0, kbuf_of(nt > 1 ? 1 : 0), kbuf_of(0), vbuf_of(0));
         if (nt > 1) {
-            step(yes{}, no{}, yes{}, 0, kbuf_of(1), kbuf_of(0), vbuf_of(0));
             retire(0);
             // middle steps, four at a time with every buffer base a constant (t = 1 mod 4 at the start of
             // each group: K_{t+1}, K_t and V_{t-1} sit in buffers 2, 1 and 0, then 3, 2, 1, ...)
@@ -974,8 +984,6 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
                 retire(t);
             }
             step(yes{}, yes{}, no{}, t, kbuf_of(t), kbuf_of(t), vbuf_of(t - 1));   // no next S
-        } else {
-            step(yes{}, no{}, no{}, 0, kbuf_of(0), kbuf_of(0), vbuf_of(0));
         }
         // P.V of the last tile, after the barrier that ends its step: that barrier is what makes the last V
         // tile visible (every wave waited for its loads of it), and it does not reload that V buffer

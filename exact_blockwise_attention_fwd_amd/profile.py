@@ -39,6 +39,13 @@ FWD_SOURCE = "attn_fwd_bf16.hip"
 BF16_PEAK_TFLOPS = 2516.6
 HBM_PEAK_GBS = 8000.0
 COPY_BYTES = 1 << 30
+# Timed and warmup steps of the trace run per workload: short workloads take more steps, so that the engine
+# clock has settled and the timed region lasts tens of milliseconds (with 3 steps a 1 ms launch reads up to
+# 25 % slow).  The counter passes use COUNTER_WARMUP warmup steps before the one step they summarise.
+TRACE_STEPS = {"ring_share_128k": (5, 2), "ulysses_share_256k": (3, 1), "causal_prefill_4k": (300, 100),
+               "peaky_16k": (100, 30), "tiny_fp32": (400, 100)}
+COUNTER_WARMUP = {"ring_share_128k": 1, "ulysses_share_256k": 1, "causal_prefill_4k": 100, "peaky_16k": 30,
+                  "tiny_fp32": 100}
 SQ_COUNTERS = ["GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
                "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS", "SQ_INSTS_VALU",
                "SQ_INSTS_MFMA", "SQ_BUSY_CU_CYCLES"]
@@ -113,6 +120,8 @@ def short(name: str) -> str:
     name = name.replace("(anonymous namespace)::", "").replace("attn::", "")
     if name.startswith("void "):
         name = name[5:]
+    if name.startswith("at::") and "<" in name:   # torch's own kernels: the template arguments run to pages
+        return name[:name.index("<")] + "<…>"
     depth = 0
     for i, ch in enumerate(name):   # cut at the argument list: the first '(' outside template brackets
         if ch == "<":
@@ -157,7 +166,7 @@ def launch_flops(w) -> list[float]:
     return [f * w.flops() / tot for f in out] if tot else out
 
 
-def trace(names: list[str], raw: str, steps: int, warmup: int) -> str:
+def trace(names: list[str], raw: str, steps_override: int | None, warmup_override: int | None) -> str:
     fpr = fingerprint()
     lines = ["# Kernel trace of the attention kernels, every configured workload", "",
              f"Forward kernel build fingerprint (source and compile flags): `{fpr}`", "",
@@ -168,6 +177,9 @@ def trace(names: list[str], raw: str, steps: int, warmup: int) -> str:
     machine = []
     for n in names:
         w = workload(n)
+        steps, warmup = TRACE_STEPS.get(n, (3, 2))
+        steps = steps_override or steps
+        warmup = warmup if warmup_override is None else warmup_override
         out, shown = run_profiled(f"trace_{n}", ["--kernel-trace", "--stats"],
                                   ["--workload", n, "--steps", str(steps), "--warmup", str(warmup), "--no-cpu-baseline",
                                    "--no-streamed", "--no-graph", "--no-ffn", "--no-ulysses"], raw, 300)
@@ -267,8 +279,8 @@ def traffic(name: str, raw: str) -> str:
 def counters(name: str, raw: str) -> str:
     fpr = fingerprint()
     w = workload(name)
-    args = ["--workload", name, "--steps", "1", "--warmup", "1", "--no-cpu-baseline", "--no-streamed", "--no-graph",
-            "--no-ffn", "--no-ulysses"]
+    args = ["--workload", name, "--steps", "1", "--warmup", str(COUNTER_WARMUP.get(name, 1)), "--no-cpu-baseline",
+            "--no-streamed", "--no-graph", "--no-ffn", "--no-ulysses"]
     out, shown = run_profiled(f"counters_{name}", ["--pmc", *SQ_COUNTERS], args, raw, 150)
     rows = read_csv(out, "counter_collection.csv")
     disp = {}
@@ -278,8 +290,7 @@ def counters(name: str, raw: str) -> str:
             continue
         d = disp.setdefault(int(col(r, "Correlation_Id", "Dispatch_Id")), {"kernel": k})
         d[col(r, "Counter_Name")] = float(col(r, "Counter_Value"))
-        for key, names in (("start", ("Start_Timestamp",)), ("end", ("End_Timestamp",)), ("scratch", ("Scratch_Size",)),
-                           ("vgpr", ("VGPR_Count", "Arch_VGPR_Count")), ("agpr", ("Accum_VGPR_Count",))):
+        for key, names in (("start", ("Start_Timestamp",)), ("end", ("End_Timestamp",)), ("scratch", ("Scratch_Size",))):
             try:
                 d[key] = float(col(r, *names))
             except (KeyError, ValueError):
@@ -294,9 +305,11 @@ def counters(name: str, raw: str) -> str:
              "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GUI cycles x 1024); MFMA FLOP / algorithmic = SQ_INSTS_VALU_MFMA_MOPS_BF16",
              "x 512 / (4 d per visible pair); co-issue = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES; VALU / MFMA",
              "and LDS / MFMA = SQ_INSTS_VALU (MFMAs included) and SQ_INSTS_LDS per SQ_INSTS_MFMA; LDS conflict =",
-             "SQ_LDS_BANK_CONFLICT / (GUI cycles x 256).", "",
+             "SQ_LDS_BANK_CONFLICT / (GUI cycles x 256); scratch = the dispatch record's private bytes per lane.",
+             "Registers are in kernel_resource_usage.txt (the compiler's counts; the dispatch record's VGPR field",
+             "reads 128 for the 256-VGPR kernels and is not used).", "",
              "| launch | us | sclk GHz | TFLOP/s | MFMA busy | MFMA FLOP / alg. | co-issue | VALU / MFMA | LDS / MFMA | "
-             "LDS conflict | scratch B/lane | VGPR | AGPR |", "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+             "LDS conflict | scratch B/lane |", "|---|---|---|---|---|---|---|---|---|---|---|"]
     acc = {"busy": 0.0, "ratio": 0.0, "coexec": 0.0, "conf": 0.0, "sclk": 0.0, "w": 0.0}
     for i, d in enumerate(ds):
         try:
@@ -313,8 +326,7 @@ def counters(name: str, raw: str) -> str:
             continue
         tf = flops[i] / (us * 1e-6) / 1e12
         lines.append(f"| {i} | {us:.0f} | {sclk:.2f} | {tf:.0f} | {busy:.3f} | {ratio:.3f} | {co:.3f} | {vm:.2f} | {lm:.2f} | "
-                     f"{conf:.4f} | {d.get('scratch', float('nan')):.0f} | {d.get('vgpr', float('nan')):.0f} | "
-                     f"{d.get('agpr', float('nan')):.0f} |")
+                     f"{conf:.4f} | {d.get('scratch', float('nan')):.0f} |")
         wgt = flops[i]
         acc["busy"] += busy * wgt
         acc["ratio"] += ratio * wgt
@@ -335,8 +347,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--what", default="trace,traffic,counters")
     ap.add_argument("--workloads", default="ring_share_128k,ulysses_share_256k,causal_prefill_4k,peaky_16k,tiny_fp32")
-    ap.add_argument("--steps", type=int, default=3)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps of every trace run (default: per workload)")
+    ap.add_argument("--warmup", type=int, default=None, help="warmup steps of every trace run (default: per workload)")
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "profiles"))
     ap.add_argument("--raw", default=os.path.join(ROOT, "gpurun_out", "prof_raw"))
     a = ap.parse_args()
