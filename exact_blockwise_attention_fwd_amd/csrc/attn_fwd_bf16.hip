@@ -205,19 +205,29 @@ __device__ __forceinline__ void store_row(const FwdArgs& a, int bh, int qi, int 
 // t+2 is loaded into the buffers of K_t and V_{t-1}; it has a whole iteration to land.
 template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd_bf16_kernel(FwdArgs a, int num_qt,
-                                                                                            int total, int per_xcd) {
+                                                                                            int total, int per_xcd,
+                                                                                            int length_major) {
     using T = Tile<D>;
     constexpr int QB = T::QB;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     lds_char* const lds = (lds_char*)smem;   // all LDS addressing stays in the LDS address space
 
-    // XCD-aware remap: hardware workgroup w runs on XCD w % 8; give each XCD a contiguous logical range
+    // Workgroup order (as in fwd_p3_kernel): hardware workgroup w runs on XCD w % 8; equal-length tiles give
+    // each XCD a contiguous range of (head, query tile), unequal ones (a causal diagonal in the key range) go
+    // length-major, longest first across all heads.
     const int w_hw = blockIdx.x;
-    const int logical = (w_hw % NXCD) * per_xcd + w_hw / NXCD;
-    if (logical >= total) return;
-    const int bh = logical / num_qt;
-    int qt = logical % num_qt;
-    if (CAUSAL) qt = num_qt - 1 - qt;                // longest query tiles first
+    int bh, qt;
+    if (CAUSAL && length_major) {
+        if (w_hw >= total) return;
+        const int nbh = total / num_qt;
+        bh = w_hw % nbh;
+        qt = num_qt - 1 - w_hw / nbh;
+    } else {
+        const int logical = (w_hw % NXCD) * per_xcd + w_hw / NXCD;
+        if (logical >= total) return;
+        bh = logical / num_qt;
+        qt = logical % num_qt;
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -574,9 +584,10 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
     const int total = (int)total_ll;
     const int per_xcd = (total + NXCD - 1) / NXCD;
     const int grid = per_xcd * NXCD;
+    const int length_major = CAUSAL && (long long)a.offset < (long long)a.n_kv - 1;
     auto kern = fwd_bf16_kernel<D, CAUSAL, OUT_F32>;
     if (hipError_t e = allow_lds<fwd_bf16_kernel<D, CAUSAL, OUT_F32>>(T::LDS); e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(T::THREADS), T::LDS, s, a, num_qt, total, per_xcd);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(T::THREADS), T::LDS, s, a, num_qt, total, per_xcd, length_major);
     return hipGetLastError();
 }
 
@@ -618,19 +629,33 @@ struct P3 {
 };
 
 template <int NW, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, int num_qt, int total, int per_xcd) {
+__global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, int num_qt, int total, int per_xcd,
+                                                                    int length_major) {
     using T = P3<NW>;
     constexpr int D = T::D;
     constexpr int WS = T::WSTRIDE;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     lds_char* const lds = (lds_char*)smem;
 
+    // Workgroup order.  Hardware workgroup w runs on XCD w mod 8.  Tiles of equal length: each XCD takes a
+    // contiguous range of (head, query tile), so its heads' K/V streams share its L2.  Tiles of unequal length
+    // (a causal diagonal inside the key range): length-major, w takes query tile rank w / BH (longest first) of
+    // head w mod BH, so every XCD starts all of its longest tiles before any shorter one (a head-major order
+    // left long tiles of later heads to start last and run into the launch's tail); XCD x then works on the
+    // heads congruent to x mod 8.
     const int w_hw = blockIdx.x;
-    const int logical = (w_hw % NXCD) * per_xcd + w_hw / NXCD;
-    if (logical >= total) return;
-    const int bh = logical / num_qt;
-    int qt = logical % num_qt;
-    if (CAUSAL) qt = num_qt - 1 - qt;                // longest query tiles first
+    int bh, qt;
+    if (CAUSAL && length_major) {
+        if (w_hw >= total) return;
+        const int nbh = total / num_qt;
+        bh = w_hw % nbh;
+        qt = num_qt - 1 - w_hw / nbh;
+    } else {
+        const int logical = (w_hw % NXCD) * per_xcd + w_hw / NXCD;
+        if (logical >= total) return;
+        bh = logical / num_qt;
+        qt = logical % num_qt;
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1107,25 +1132,32 @@ hipError_t launch_p3(const FwdArgs& a, hipStream_t st) {
     const int total = (int)total_ll;
     const int per_xcd = (total + NXCD - 1) / NXCD;
     const int grid = per_xcd * NXCD;
+    // query tiles differ in length when some row does not see every key (row 0 sees keys up to 0 + offset)
+    const int length_major = CAUSAL && (long long)a.offset < (long long)a.n_kv - 1;
     auto kern = fwd_p3_kernel<NW, CAUSAL, OUT_F32>;
     if (hipError_t e = allow_lds<fwd_p3_kernel<NW, CAUSAL, OUT_F32>>(T::LDS); e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(T::THREADS), T::LDS, st, a, num_qt, total, per_xcd);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(T::THREADS), T::LDS, st, a, num_qt, total, per_xcd, length_major);
     return hipGetLastError();
 }
 
 }  // namespace
 
-// Workgroup size of the d = 128 kernel: eight waves (256 query rows, one workgroup per CU) when the launch
-// has at least eight such workgroups per CU, four waves (128 rows, two workgroups per CU) otherwise, where
-// smaller workgroups balance better.  ATTN_BF16_D128_WAVES=4 or 8 forces one of them (used by the tests to
-// run every shape through both).
+// Workgroup size of the d = 128 kernel.  Eight waves (256 query rows, one workgroup per CU: both waves of a
+// SIMD share each K/V tile) unless the launch has fewer such tiles than CUs, or its rows are short and causal
+// (fewer than 3072 keys), where 128-row workgroups fill the chip and balance the diagonal better.  Measured
+// against four waves with the length-major order of causal launches: +4 to +14 % on causal rows of 3072 to
+// 8192 keys, +2 to +6 % without a mask from 1 to 8 tiles per CU, -4 to -6 % on causal rows of 1024 and
+// 2048 keys at 4 tiles per CU.  ATTN_BF16_D128_WAVES=4 or 8 forces one of them (used by the tests to run
+// every shape through both).
 static int d128_waves(const FwdArgs& a) {
     if (const char* e = getenv("ATTN_BF16_D128_WAVES")) {
         const int v = atoi(e);
         if (v == 4 || v == 8) return v;
     }
     const long long wide = (long long)((a.n_q + 255) / 256) * a.bh;
-    return wide >= 8LL * device_cus() ? 8 : 4;
+    if (wide < device_cus()) return 4;
+    if (a.causal && a.n_kv < 3072) return 4;
+    return 8;
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, bool out_f32, hipStream_t s) {
