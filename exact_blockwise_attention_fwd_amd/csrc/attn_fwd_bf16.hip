@@ -943,8 +943,9 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
     // V_{t-1}; K_{t+NK} and V_{t+NV-1} then go into their buffers.  All waves run exactly ntiles such barriers.
     auto retire = [&](int t) __attribute__((always_inline)) {
         // K_{t+2} and V_t were issued L steps ago; the loads of the L-1 later retires may still fly (when
-        // all of them exist; near the end, wait for everything)
-        if (t - 1 + T::LEAD < ntiles) __builtin_amdgcn_s_waitcnt(0x0F70 | T::AFTER);
+        // all of them exist; near the end, and after step 0, whose lead loads the prologue issued in another
+        // order, wait for everything)
+        if (t > 0 && t - 1 + T::LEAD < ntiles) __builtin_amdgcn_s_waitcnt(0x0F70 | T::AFTER);
         else __builtin_amdgcn_s_waitcnt(0x0F70);
         lds_barrier();
         load_k(t + T::NK);
@@ -953,11 +954,14 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
     using yes = std::integral_constant<bool, true>;
     using no = std::integral_constant<bool, false>;
 
-    // ---- prologue: K_0, K_1, K_2 and V_0 in flight; all must land (in every wave) before S(0)
-    for (int j = 0; j < T::NK; ++j) load_k(j);
-    for (int j = 0; j < T::NV - 1; ++j) load_v(j);
+    // ---- prologue: K_0 and K_1 must land (in every wave) before S(0) and S(1); the other lead loads (K_2 ..
+    // K_{NK-1}, V_0 .. V_{NV-2}) are issued after that barrier and land under S(0) and step 0
+    load_k(0);
+    load_k(1);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     lds_barrier();
+    for (int j = 2; j < T::NK; ++j) load_k(j);
+    for (int j = 0; j < T::NV - 1; ++j) load_v(j);
 
     // Steps 0 .. nt-1 (step t: softmax of tile t, P.V of t-1, S of t+1), then the P.V of the last tile.
     const int nt = wave_tiles;
@@ -983,6 +987,20 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
     };
     if (nt > 0) {
         s_all(s, kbuf_of(0));
+        // The reference starts at tile 0's row max, taken here while its scores are still in registers, so that
+        // step 0 does not redo the tile (recomputing its scores from K_0) as a row without a reference would.
+        // A row whose tile-0 keys are all masked keeps no reference (m = -inf) and is redone as before.
+        {
+            if (0 >= full_tiles) mask_tile(0, s);
+            float mt = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) mt = fmaxf(mt, s[kb][j]);
+            m = fmaxf(mt, wave_xor32(mt));
+            mcr = m == -INFINITY ? 0.f : m * c;
+            bnd = m == -INFINITY ? -1.f : REF_BOUND;
+        }
         // Step 0: the softmax of tile 0 and S(1).  A wave with a single tile runs the same step (one call site
         // for both cases, so no second copy of the read offsets is kept across the loop) with its S part
         // recomputing the scores of tile 0, which nothing reads: its weights are already packed for P.V.

@@ -13,6 +13,8 @@ produced them and the build fingerprint of the forward kernel (its source and co
             against the dense bf16 peak, merge GB/s against the HBM peak.
   traffic   FETCH_SIZE and WRITE_SIZE (one counter per pass) per forward launch of the ring-share step and per
             merge launch, each scaled by what the same counter reads for a plain 1 GiB device-to-device copy.
+  streamed  --kernel-trace --memory-copy-trace over the host-streamed step: chunk copies (count, bytes, GB/s)
+            and kernel durations.
   counters  GRBM_GUI_ACTIVE and SQ counters per forward launch: MFMA busy fraction, effective engine clock,
             MFMA FLOP per algorithmic FLOP, VALU co-issue beside MFMA, VALU and LDS instructions per MFMA, LDS
             bank conflicts, and the scratch (spill) bytes per lane the dispatch ran with.
@@ -343,9 +345,60 @@ def counters(name: str, raw: str) -> str:
     return "\n".join(lines)
 
 
+# ------------------------------------------------------------------------------------------- host streaming
+def streamed(raw: str) -> str:
+    """Kernel and memory-copy trace of the bench's host-streamed step (K and V in page-locked host memory, each
+    chunk copied on a second stream while the previous chunk computes): the chunk copies' count, duration and
+    bytes, and the kernels' durations, next to the bench's own streamed figures."""
+    fpr = fingerprint()
+    args = ["--workload", "ring_share_128k", "--steps", "3", "--warmup", "1", "--no-cpu-baseline", "--no-graph",
+            "--no-ffn", "--no-ulysses"]
+    out, shown = run_profiled("streamed_ring_share_128k", ["--kernel-trace", "--memory-copy-trace", "--stats"], args,
+                              raw, 300)
+    lines = ["# Host-streamed chunked step, ring_share_128k: kernel and memory-copy trace", "",
+             f"Forward kernel build fingerprint: `{fpr}`", "",
+             "K and V (1 GiB each) sit in page-locked host memory; each chunk's K rows and V rows (128 MiB each, one",
+             "2-D copy per tensor) go to one of two staging slots on a copy stream while the previous chunk computes.",
+             "The profiled bench runs the device-resident step (1 warmup + 3 timed), the stand-alone merge (12",
+             "launches), then the streamed step (1 warmup + 5 timed).", "", "Command:", "", f"    {shown}", ""]
+    b = bench_json(out)
+    if b and b.get("streamed"):
+        st = b["streamed"]
+        lines += [f"bench line under the profiler: streamed {st.get('ms_per_step')} ms per step, copies "
+                  f"{st.get('copy_ms_per_step')} ms at {st.get('h2d_gbs')} GB/s, device-resident "
+                  f"{st.get('device_resident_ms_per_step')} ms, overlap efficiency {st.get('overlap_efficiency')}", ""]
+    tr = read_csv(out, "memory_copy_trace.csv")
+    if tr:
+        size_key = next((k for k in tr[0] if k.lower() in ("bytes", "size", "copy_bytes")), None)
+        dir_key = next((k for k in tr[0] if k.lower() in ("direction", "operation", "kind")), None)
+        groups = {}
+        for r in tr:
+            nbytes = int(float(r[size_key])) if size_key else -1
+            kind = r[dir_key] if dir_key else "copy"
+            us = (int(col(r, "End_Timestamp")) - int(col(r, "Start_Timestamp"))) * 1e-3
+            g = groups.setdefault((kind, nbytes), [])
+            g.append(us)
+        lines += ["Memory copies (`memory_copy_trace.csv`), grouped by kind and size:", "",
+                  "| kind | bytes per copy | copies | average us | GB/s |", "|---|---|---|---|---|"]
+        for (kind, nbytes), us in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            avg = sum(us) / len(us)
+            gbs = f"{nbytes / (avg * 1e3):.1f}" if nbytes > 0 and avg > 0 else "-"
+            lines.append(f"| {kind} | {nbytes if nbytes >= 0 else '-'} | {len(us)} | {avg:.1f} | {gbs} |")
+        if not size_key:
+            lines += ["", "(columns of the copy trace: " + ", ".join(tr[0].keys()) + ")"]
+        lines.append("")
+    stats = read_csv(out, "kernel_stats.csv")
+    lines += ["Kernels (`kernel_stats.csv`):", "", "| kernel | calls | average us | total ms |", "|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(col(r, "TotalDurationNs"))):
+        lines.append(f"| `{short(col(r, 'Name', 'Kernel_Name'))}` | {col(r, 'Calls')} | "
+                     f"{float(col(r, 'AverageNs')) / 1e3:.1f} | {float(col(r, 'TotalDurationNs')) / 1e6:.2f} |")
+    lines.append("")
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--what", default="trace,traffic,counters")
+    ap.add_argument("--what", default="trace,traffic,counters,streamed")
     ap.add_argument("--workloads", default="ring_share_128k,ulysses_share_256k,causal_prefill_4k,peaky_16k,tiny_fp32")
     ap.add_argument("--steps", type=int, default=None, help="timed steps of every trace run (default: per workload)")
     ap.add_argument("--warmup", type=int, default=None, help="warmup steps of every trace run (default: per workload)")
@@ -362,6 +415,9 @@ def main():
     if "traffic" in what:
         open(os.path.join(a.out, "attn_fwd_bf16_traffic.txt"), "w").write(traffic("ring_share_128k", a.raw))
         log("wrote attn_fwd_bf16_traffic.txt")
+    if "streamed" in what:
+        open(os.path.join(a.out, "attn_fwd_streamed_ring_share_128k.md"), "w").write(streamed(a.raw))
+        log("wrote attn_fwd_streamed_ring_share_128k.md")
     if "counters" in what:
         for n in names:
             if workload(n).dtype != "bf16":
