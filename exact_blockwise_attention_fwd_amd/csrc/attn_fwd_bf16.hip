@@ -141,6 +141,15 @@ __device__ __forceinline__ float add_bf16_pair(unsigned a, float acc) {
 // arrives.  Tile loads into LDS that are still in flight are not waited for here (a release fence would
 // wait for all of them); callers wait with an explicit vmcnt for exactly the loads that must have landed.
 // The empty asm statements keep the compiler from moving memory accesses across the barrier.
+// As lds_barrier, but the last four LDS reads of the wave may still be in flight (in-order LDS returns): the
+// prefetched first V operands of the next step, from a buffer no load issued after the barrier overwrites.
+__device__ __forceinline__ void lds_barrier_keep4() {
+    __builtin_amdgcn_s_waitcnt(0xC47F);   // lgkmcnt(4)
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     __asm__ volatile("" ::: "memory");
@@ -604,7 +613,10 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
 // exponent reference rule in the file header) recomputes its scores from K_t, which stays in LDS until
 // the step ends.  Two waves share every SIMD.  A workgroup is either four waves (128 query rows) or eight
 // (256 rows: both waves of each SIMD then belong to it and share its K/V tiles, and with one workgroup per
-// CU the LDS holds three steps of lead for every load).  K_{t+NK} and V_{t+NV-1} are loaded when step t ends.
+// CU the LDS holds four K and four V buffers).  K_{t+NK} and V_{t+NV-1} are loaded when step t ends.  With
+// eight waves V_{t+1} is waited for at the end of step t, one step before its P.V, so that each step can
+// read the next step's first two V^T operands before its barrier and the next P.V starts without waiting
+// for LDS.
 template <int NW_>
 struct P3 {
     static constexpr int D = 128, NW = NW_, THREADS = 64 * NW, BR = 32 * NW, BC = 64;
@@ -619,7 +631,11 @@ struct P3 {
     // retire(t) needs K_{t+2} (issued by retire(t+2-NK)) and V_t (by retire(t+1-NV)) to have landed; loads
     // are issued K then V per retire, and this many load instructions issued after the later of the two
     // may still be in flight
-    static constexpr int DK = NK - 2, DV = NV - 1;
+    // VAHEAD: eight-wave steps read the first V operands of the next step before the barrier that ends
+    // them, so V_{t+1} must have landed (in every wave) by retire(t) already
+    static constexpr int VAHEAD = NW == 8 ? 1 : 0;
+    static constexpr int DK = NK - 2, DV = NV - 1 - VAHEAD;
+    static_assert(DV >= 1, "V is loaded at least one step before it is needed");
     static constexpr int AFTER = (DK < DV ? 1 + 2 * (DK - 1) : 2 * (DV - 1)) * SEGS_PER_WAVE;
     static constexpr int LEAD = NK > NV - 1 ? NK : NV - 1;   // all loads up to retire(t-1) exist iff t-1+LEAD < ntiles
     static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
@@ -825,8 +841,10 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
     // pointers distinct from the buffers the loads issued at the step's end write (K_{t+NK}, V_{t+NV-1}), so
     // the compiler does not wait for those loads before reading; the explicit vmcnt wait before every
     // barrier is what makes that true.
+    i16x4 vpl[2], vph[2];   // the first two V^T operands of the next step's P.V, read before the barrier
     auto step = [&](auto do_soft, auto do_pv, auto do_s, int t, const lds_char* __restrict__ kn,
-                    const lds_char* __restrict__ kc, const lds_char* __restrict__ vp) __attribute__((always_inline)) {
+                    const lds_char* __restrict__ kc, const lds_char* __restrict__ vp,
+                    const lds_char* __restrict__ vnx) __attribute__((always_inline)) {
         constexpr bool SOFT = decltype(do_soft)::value, PV = decltype(do_pv)::value, S = decltype(do_s)::value;
         // The per-lane LDS offsets pass through an empty statement, so that "buffer + offset" is formed once
         // per offset and step and the (kb, ks) constants land in the reads' offset fields.
@@ -864,8 +882,15 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
                 vhh[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q + 4 * T::ROW));
             };
             if constexpr (PV) {
-                vread(0);
-                vread(1);
+                if constexpr (T::VAHEAD) {
+                    vl[0] = vpl[0];
+                    vhh[0] = vph[0];
+                    vl[1] = vpl[1];
+                    vhh[1] = vph[1];
+                } else {
+                    vread(0);
+                    vread(1);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -944,6 +969,15 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
             }
             l = __builtin_fmaf(l, alpha, rs);
         }
+        if constexpr (SOFT && T::VAHEAD) {
+            // the next step's first two V^T operands (V_t, landed by the previous retire), under this barrier
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const lds_char* q = vnx + v_roff[i];
+                vpl[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)q);
+                vph[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q + 4 * T::ROW));
+            }
+        }
     };
     // End of step t: every wave's loads of K_{t+2} and V_t have landed and every wave is done with K_t and
     // V_{t-1}; K_{t+NK} and V_{t+NV-1} then go into their buffers.  All waves run exactly ntiles such barriers.
@@ -953,7 +987,8 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
         // order, wait for everything)
         if (t > 0 && t - 1 + T::LEAD < ntiles) __builtin_amdgcn_s_waitcnt(0x0F70 | T::AFTER);
         else __builtin_amdgcn_s_waitcnt(0x0F70);
-        lds_barrier();
+        if constexpr (T::VAHEAD) lds_barrier_keep4();
+        else lds_barrier();
         load_k(t + T::NK);
         load_v(t + T::NV - 1);
     };
@@ -964,10 +999,11 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
     // K_{NK-1}, V_0 .. V_{NV-2}) are issued after that barrier and land under S(0) and step 0
     load_k(0);
     load_k(1);
+    if constexpr (T::VAHEAD) load_v(0);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     lds_barrier();
     for (int j = 2; j < T::NK; ++j) load_k(j);
-    for (int j = 0; j < T::NV - 1; ++j) load_v(j);
+    for (int j = T::VAHEAD; j < T::NV - 1; ++j) load_v(j);
 
     // Steps 0 .. nt-1 (step t: softmax of tile t, P.V of t-1, S of t+1), then the P.V of the last tile.
     const int nt = wave_tiles;
@@ -1010,7 +1046,7 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
         // Step 0: the softmax of tile 0 and S(1).  A wave with a single tile runs the same step (one call site
         // for both cases, so no second copy of the read offsets is kept across the loop) with its S part
         // recomputing the scores of tile 0, which nothing reads: its weights are already packed for P.V.
-        step(yes{}, no{}, yes{}, 0, kbuf_of(nt > 1 ? 1 : 0), kbuf_of(0), vbuf_of(0));
+        step(yes{}, no{}, yes{}, 0, kbuf_of(nt > 1 ? 1 : 0), kbuf_of(0), vbuf_of(0), vbuf_of(0));
         if (nt > 1) {
             retire(0);
             // middle steps, four at a time with every buffer base a constant (t = 1 mod 4 at the start of
@@ -1023,16 +1059,16 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
                     for (int u = 0; u < 4; ++u) {
                         const int ph = (1 + u) & 3;   // t + u mod 4
                         step(yes{}, yes{}, yes{}, t + u, lds_at(((ph + 1) & 3) * T::TILE), lds_at(ph * T::TILE),
-                             lds_at(((ph + 3) & 3) * T::TILE));
+                             lds_at(((ph + 3) & 3) * T::TILE), lds_at(ph * T::TILE));
                         retire(t + u);
                     }
                 }
             }
             for (; t < nt - 1; ++t) {
-                step(yes{}, yes{}, yes{}, t, kbuf_of(t + 1), kbuf_of(t), vbuf_of(t - 1));
+                step(yes{}, yes{}, yes{}, t, kbuf_of(t + 1), kbuf_of(t), vbuf_of(t - 1), vbuf_of(t));
                 retire(t);
             }
-            step(yes{}, yes{}, no{}, t, kbuf_of(t), kbuf_of(t), vbuf_of(t - 1));   // no next S
+            step(yes{}, yes{}, no{}, t, kbuf_of(t), kbuf_of(t), vbuf_of(t - 1), vbuf_of(t));   // no next S
         }
         // P.V of the last tile, after the barrier that ends its step: that barrier is what makes the last V
         // tile visible (every wave waited for its loads of it), and it does not reload that V buffer
@@ -1040,7 +1076,7 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
         ++t;
         // the running partial is loaded now, to arrive during the last P.V
         if (a.o_prev) fetch_prev();
-        step(no{}, yes{}, no{}, t, kbuf_of(t), kbuf_of(t), vbuf_of(nt - 1));
+        step(no{}, yes{}, no{}, t, kbuf_of(t), kbuf_of(t), vbuf_of(nt - 1), vbuf_of(nt - 1));
     } else if (a.o_prev) {
         fetch_prev();
     }
