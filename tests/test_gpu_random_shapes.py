@@ -1,0 +1,77 @@
+"""GPU parity on seeded random shapes: combinations of batch, heads, query and key counts, head dimension,
+dtype, causal mask, logit spread and chunk count that the hand-picked shapes do not cover, each compared in
+full against the fp64 oracle ("FlashAttention by hand", paragraphs on online softmax and the loop with its
+single division; chunks folded as in the "ATTENTION2D" explainer, section 2).
+
+The cases are drawn once from a fixed seed, so the set is the same on every run.  Sizes stay where the
+oracle finishes in well under a second per case while still spanning several key tiles with ragged tails.
+For d = 128 in bf16 every case also fixes the workgroup size (four or eight waves) through
+ATTN_BF16_D128_WAVES, alternating, so that both d = 128 kernels meet shapes the launch heuristic would not
+hand them: query counts below one workgroup, key counts below one tile, causal launches whose rows see no key.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import exact_blockwise_attention_fwd_amd as A
+import oracle
+import workloads as W
+from parity import assert_parity, errors, out_to_f64, storage_to_f64, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _cases(n: int = 60):
+    rng = np.random.default_rng(20261203)
+    out = []
+    for i in range(n):
+        dt = "bf16" if i % 4 != 3 else "f32"
+        d = int(rng.choice([128, 64])) if dt == "bf16" else int(rng.choice([64, 37, 128, 16]))
+        B = int(rng.integers(1, 3))
+        H = int(rng.integers(1, 7))
+        N_q = int(rng.choice([int(rng.integers(1, 64)), int(rng.integers(64, 700))]))
+        N_kv = int(rng.choice([int(rng.integers(1, 64)), int(rng.integers(64, 1500))]))
+        causal = bool(rng.integers(0, 2))
+        q_std = float(rng.choice([1.0, 1.0, 3.0]))
+        chunks = int(rng.choice([1, 1, 2, 5]))
+        waves = ("4" if i % 2 else "8") if (dt == "bf16" and d == 128) else None
+        out.append((B, H, N_q, N_kv, d, dt, causal, q_std, chunks, waves))
+    return out
+
+
+CASES = _cases()
+
+
+def _id(c):
+    B, H, N_q, N_kv, d, dt, causal, q_std, chunks, waves = c
+    return (f"{B}x{H}x{N_q}x{N_kv}d{d}{dt}{'c' if causal else 'n'}q{q_std:g}p{chunks}" +
+            (f"w{waves}" if waves else ""))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    A.lib()
+
+
+@pytest.mark.parametrize("case", CASES, ids=_id)
+def test_random_shape(case, monkeypatch):
+    B, H, N_q, N_kv, d, dt, causal, q_std, chunks, waves = case
+    if waves:
+        monkeypatch.setenv("ATTN_BF16_D128_WAVES", waves)
+    w = W.Workload("random", B, H, N_q, N_kv, d, dt, causal, chunks,
+                   seed=7000 + CASES.index(case), q_std=q_std)
+    st = [W.tensor_storage(w, t) for t in (W.Q_T, W.K_T, W.V_T)]
+    q, k, v = (to_device(s) for s in st)
+    o_ref, l_ref = oracle.attention(*(storage_to_f64(s) for s in st), w.scale, causal, w.offset)
+    if chunks == 1:
+        o, lse = A.fwd(q, k, v, causal=causal, scale=w.scale)
+    else:
+        o, lse = A.fwd_chunked(q, k, v, chunks, causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    err = errors(out_to_f64(o), out_to_f64(lse), o_ref, l_ref)
+    print(_id(case), err, flush=True)
+    assert_parity(err, dt, _id(case))
