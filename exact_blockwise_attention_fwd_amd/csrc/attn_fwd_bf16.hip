@@ -141,17 +141,18 @@ __device__ __forceinline__ float add_bf16_pair(unsigned a, float acc) {
 // arrives.  Tile loads into LDS that are still in flight are not waited for here (a release fence would
 // wait for all of them); callers wait with an explicit vmcnt for exactly the loads that must have landed.
 // The empty asm statements keep the compiler from moving memory accesses across the barrier.
-// As lds_barrier, but the last four LDS reads of the wave may still be in flight (in-order LDS returns): the
-// prefetched first V operands of the next step, from a buffer no load issued after the barrier overwrites.
-__device__ __forceinline__ void lds_barrier_keep4() {
-    __builtin_amdgcn_s_waitcnt(0xC47F);   // lgkmcnt(4)
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+// As lds_barrier, but the wave's last four LDS reads may still be in flight (LDS reads return in order): the
+// next step's first V^T operands, read from a buffer that no load issued after this barrier overwrites.  Every
+// other read of the step has completed, since its value was consumed before the wave reached the barrier.
+__device__ __forceinline__ void lds_barrier_keep4() {
+    __builtin_amdgcn_s_waitcnt(0xC47F);   // lgkmcnt(4)
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
@@ -628,11 +629,10 @@ struct P3 {
     static constexpr int EXTRA = NK + NV >= NW + 1 ? 0 : NW + 1 - NK - NV;   // staging-only buffers
     static constexpr int LDS = (NK + NV + EXTRA) * TILE;
     static constexpr int WSTRIDE = NW * RPS * ROW;   // bytes between the load segments of one wave
-    // retire(t) needs K_{t+2} (issued by retire(t+2-NK)) and V_t (by retire(t+1-NV)) to have landed; loads
-    // are issued K then V per retire, and this many load instructions issued after the later of the two
-    // may still be in flight
-    // VAHEAD: eight-wave steps read the first V operands of the next step before the barrier that ends
-    // them, so V_{t+1} must have landed (in every wave) by retire(t) already
+    // retire(t) needs K_{t+2} (issued by retire(t+2-NK)) and V_{t+VAHEAD} (by retire(t+VAHEAD+1-NV)) to have
+    // landed; loads are issued K then V per retire, and AFTER load instructions issued after the later of the
+    // two may still be in flight.  VAHEAD = 1: eight-wave steps read the first V operands of the next step
+    // before the barrier that ends them, so V_{t+1} must have landed (in every wave) by retire(t) already
     static constexpr int VAHEAD = NW == 8 ? 1 : 0;
     static constexpr int DK = NK - 2, DV = NV - 1 - VAHEAD;
     static_assert(DV >= 1, "V is loaded at least one step before it is needed");
@@ -979,10 +979,11 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
             }
         }
     };
-    // End of step t: every wave's loads of K_{t+2} and V_t have landed and every wave is done with K_t and
-    // V_{t-1}; K_{t+NK} and V_{t+NV-1} then go into their buffers.  All waves run exactly ntiles such barriers.
+    // End of step t: every wave's loads of K_{t+2} and V_{t+VAHEAD} have landed and every wave is done with K_t
+    // and V_{t-1}; K_{t+NK} and V_{t+NV-1} then go into their buffers.  All waves run exactly ntiles such
+    // barriers.
     auto retire = [&](int t) __attribute__((always_inline)) {
-        // K_{t+2} and V_t were issued L steps ago; the loads of the L-1 later retires may still fly (when
+        // K_{t+2} and V_{t+VAHEAD} were issued steps ago; the loads of the later retires may still fly (when
         // all of them exist; near the end, and after step 0, whose lead loads the prologue issued in another
         // order, wait for everything)
         if (t > 0 && t - 1 + T::LEAD < ntiles) __builtin_amdgcn_s_waitcnt(0x0F70 | T::AFTER);
