@@ -33,21 +33,47 @@ CODEGEN_FLAGS = [
 HIPCC_FLAGS = CODEGEN_FLAGS + ["-I", INCLUDE, "-I", CSRC]
 
 
-# Per-source additions.  The bf16 attention kernels are scheduled with the machine scheduler's
-# memory-clause strategy: the order between MFMA batches is pinned in the source, and inside each batch this
-# strategy measured bit-identical results at +0.6-0.8 % on the d = 128 kernel and +3-4 % on the d = 64 kernel
-# (the max-ILP strategies were slower on short causal rows and on d = 64).
+# Per-source additions.  The bf16 attention kernel is scheduled with the machine scheduler's memory-clause
+# strategy: the order between MFMA batches is pinned in the source, and inside each batch this strategy
+# measured bit-identical results at +0.6-0.8 % at d = 128 (the max-ILP strategies were slower on short causal
+# rows); at d = 64 the strategies measure the same within 0.5 %.
 SOURCE_FLAGS = {
     "attn_fwd_bf16.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
 }
 
 
+def code_text(text: str) -> str:
+    """C/C++ source with its comments removed and every run of whitespace made one space: what the compiler
+    sees of it, up to layout (string and character literals are kept as written)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def fingerprint(src: str) -> str:
-    """sha256 of a source file and the code-generation flags it is compiled with (include paths left out,
-    as they differ between machines): recorded counter figures are valid only for the build they name."""
+    """sha256 of a source file's code (comments and layout left out) and the code-generation flags it is
+    compiled with (include paths left out, as they differ between machines): recorded counter figures are
+    valid only for the build they name, and a change to a comment does not make another build."""
     import hashlib
 
-    h = hashlib.sha256(open(os.path.join(CSRC, src), "rb").read())
+    h = hashlib.sha256(code_text(open(os.path.join(CSRC, src)).read()).encode())
     h.update(("\n" + " ".join(CODEGEN_FLAGS + SOURCE_FLAGS.get(src, []))).encode())
     return h.hexdigest()
 

@@ -8,9 +8,8 @@
 //
 // Mapping to CDNA4 (gfx950), designed for this chip rather than taken from the pages' GPU:
 //  * Every wave owns 32 query rows of one (b, h), and every SIMD runs two waves.  Key tiles are 64 keys
-//    for d = 128 and 128 keys for d = 64 (16 KiB of K and of V per tile either way).  Two kernels share
-//    the machinery below and differ in their software pipeline: fwd_bf16_kernel (used for d = 64) and
-//    fwd_p3_kernel (d = 128), described where each is defined.
+//    (16 KiB of K and of V per tile at d = 128, 8 KiB at d = 64).  One kernel, fwd_p3_kernel, serves both
+//    head dimensions with a three-stage software pipeline described where it is defined.
 //  * Everything is computed transposed.  S^T = K Q^T uses v_mfma_f32_32x32x16_bf16 with A = K rows from
 //    LDS and B = Q^T held in registers for the whole key loop.  In the 32x32 accumulator layout a lane then
 //    holds 16 keys of ONE query (lane l and l^32 share query l%32), so the row max and row sum are in-lane
@@ -37,13 +36,13 @@
 //    then at most 2^64, the fp32 sums stay far from overflow, and the single final division by the
 //    denominator accumulated against the same reference gives the running-max result up to rounding.
 //    The common path therefore has no row max, no rescale factor and no rescale of the accumulators.
-//  * The P.V products accumulate the weights rounded to bf16 (up to 2^-8 relative each).  The d = 64 kernel
-//    keeps two denominators per row: the fp32 sum of the weights, for the LSE, and the fp32 sum of their
-//    bf16 roundings (one v_dot2c_f32_bf16 per pair), by which it divides O, so a row's output is a convex
-//    combination of V rows with weights proportional to exactly the accumulated values and a dominant
-//    weight's rounding cancels.  The d = 128 kernel divides O by the fp32 sum (no extra instruction per
-//    pair): its O then carries the dominant weights' rounding, at most 2^-8 of the largest |V| entry in
-//    a row dominated by one key, and averaging out over rows spread across many keys.
+//  * The P.V products accumulate the weights rounded to bf16 (up to 2^-8 relative each).  At d = 64 the
+//    kernel keeps two denominators per row: the fp32 sum of the weights, for the LSE, and the fp32 sum of
+//    their bf16 roundings (one v_dot2c_f32_bf16 per pair), by which it divides O, so a row's output is a
+//    convex combination of V rows with weights proportional to exactly the accumulated values and a
+//    dominant weight's rounding cancels.  At d = 128 it divides O by the fp32 sum (no extra instruction per
+//    pair): O then carries the dominant weights' rounding, at most 2^-8 of the largest |V| entry in a row
+//    dominated by one key, and averaging out over rows spread across many keys.
 //  * Workgroup ids are remapped so that consecutive logical tiles (same head, neighbouring query rows,
 //    hence the same K/V stream) land on the same XCD and share its L2; causal launches start with the
 //    longest query tiles.
@@ -78,31 +77,6 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float REF_BOUND = 18446744073709551616.0f;   // 2^64: largest weight sum taken against a stale reference
 constexpr int NXCD = 8;
 constexpr unsigned BUF_RSRC_WORD3 = 0x00020000u;   // raw buffer, 32-bit data format, bounds-checked
-
-template <int D>
-struct Tile {
-    static constexpr int QB = 1;      // 32-row query blocks per wave
-    static constexpr int NW = 4;                     // waves per workgroup
-    static constexpr int THREADS = 64 * NW;
-    static constexpr int WAVES_PER_SIMD = 2;
-    static constexpr int BR = 32 * QB * NW;          // query rows per workgroup
-    static constexpr int BC = D == 128 ? 64 : 128;   // keys per tile
-    static constexpr int NKB = BC / 32;              // 32-key blocks of S^T per tile
-    static constexpr int NDB = D / 32;               // 32-row blocks of O^T
-    static constexpr int NKS = D / 16;               // k-steps of S^T (over d)
-    static constexpr int ROW = 2 * D;                // bytes per K or V row in LDS
-    static constexpr int TILE = BC * ROW;            // bytes of one K (or V) tile
-    static constexpr int SEGS = TILE / 1024;         // 1 KiB load segments per tile
-    static constexpr int SEGS_PER_WAVE = SEGS / NW;
-    static constexpr int RPS = 1024 / ROW;           // rows per segment
-    static constexpr int LPR = ROW / 16;             // lanes (16-byte chunks) per row
-    static constexpr int L = 2;                      // tiles of lookahead: tile t+L is loaded when iteration t ends
-    static constexpr int NK = L, NV = L + 1;         // K and V buffers (V_{t-1} is still read in iteration t)
-    static constexpr int LPT = 2 * SEGS_PER_WAVE;
-    static constexpr int LDS = (NK + NV) * TILE;
-    static_assert(SEGS % NW == 0, "segments split evenly over the waves");
-    static_assert(NW * RPS * ROW == 4096, "a wave's load segments are 4 KiB apart");
-};
 
 // bits 2 and 3 of a row index swapped (an involution)
 __device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
@@ -158,416 +132,6 @@ __device__ __forceinline__ void lds_barrier_keep4() {
     __asm__ volatile("" ::: "memory");
 }
 
-// One query row's result from a bf16 kernel: O = acc / lt and lse = m*|scale| + ln(l), or (0, -inf) when the
-// row saw no key (l is the fp32 sum of the weights, lt the fp32 sum of their bf16 roundings, which are what
-// acc accumulated); when the launch accumulates, folded into the running partial with the two-term merge
-// (M = max of the two lse, weights exp(lse - M) normalised to sum 1, lse = M + ln of their sum).  Lane h
-// of the row's half-wave pair holds head-dim elements 32*db + 8*g + 4*h + (0..3) of acc[db].
-template <int NDB, bool OUT_F32>
-__device__ __forceinline__ void store_row(const FwdArgs& a, int bh, int qi, int h, const f32x16 (&acc)[NDB],
-                                          float l_tot, float lt_tot, float m, float scale_abs) {
-    constexpr int D = 32 * NDB;
-    const float lb = l_tot > 0.f ? m * scale_abs + logf(l_tot) : -INFINITY;
-    float cb = l_tot > 0.f && lt_tot > 0.f ? 1.f / lt_tot : 0.f;   // factor on this launch's accumulator
-    float ca = 0.f;                               // factor on the previous partial
-    float lse = lb;
-    const float* op = nullptr;
-    if (a.o_prev) {
-        const float la = a.lse_prev[(size_t)bh * a.n_q + qi];
-        const float big = fmaxf(la, lb);
-        if (big != -INFINITY) {
-            const float wa = expf(la - big), wb = expf(lb - big);
-            const float inv = 1.f / (wa + wb);
-            ca = wa * inv;
-            cb *= wb * inv;
-            lse = big + logf(wa + wb);
-        } else {
-            cb = 0.f;
-            lse = -INFINITY;
-        }
-        op = a.o_prev + (size_t)bh * a.q_head_stride + (size_t)qi * D;
-    }
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int c0 = 32 * db + 8 * g + 4 * h;
-            f32x4 o4 = {acc[db][4 * g] * cb, acc[db][4 * g + 1] * cb, acc[db][4 * g + 2] * cb, acc[db][4 * g + 3] * cb};
-            if (op) {
-                o4 += ca * *reinterpret_cast<const f32x4*>(op + c0);
-            }
-            if (OUT_F32) {
-                float* oh = static_cast<float*>(a.o) + (size_t)bh * a.q_head_stride + (size_t)qi * D;
-                *reinterpret_cast<f32x4*>(oh + c0) = o4;
-            } else {
-                uint16_t* oh = static_cast<uint16_t*>(a.o) + (size_t)bh * a.q_head_stride + (size_t)qi * D;
-                const u32x2 o2 = {pack_bf16(o4[0], o4[1]), pack_bf16(o4[2], o4[3])};
-                *reinterpret_cast<u32x2*>(oh + c0) = o2;
-            }
-        }
-    if (h == 0) a.lse[(size_t)bh * a.n_q + qi] = lse;
-}
-
-// ---- Two-stage pipeline (used for d = 64): workgroups of four waves (128 query rows), two per CU.  K is
-// double-buffered and V triple-buffered.  Iteration t computes S(t) and the weights of tile t, and the P.V
-// product of tile t-1: the softmax of one tile shares a basic block with the P.V MFMAs of the previous one,
-// so the VALU and the matrix cores overlap inside one wave.  After the barrier that ends iteration t, tile
-// t+2 is loaded into the buffers of K_t and V_{t-1}; it has a whole iteration to land.
-template <int D, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(Tile<D>::THREADS, Tile<D>::WAVES_PER_SIMD) void fwd_bf16_kernel(FwdArgs a, int num_qt,
-                                                                                            int total, int per_xcd,
-                                                                                            int length_major) {
-    using T = Tile<D>;
-    constexpr int QB = T::QB;
-    extern __shared__ __attribute__((aligned(1024))) char smem[];
-    lds_char* const lds = (lds_char*)smem;   // all LDS addressing stays in the LDS address space
-
-    // Workgroup order (as in fwd_p3_kernel): hardware workgroup w runs on XCD w % 8; equal-length tiles give
-    // each XCD a contiguous range of (head, query tile), unequal ones (a causal diagonal in the key range) go
-    // length-major, longest first across all heads.
-    const int w_hw = blockIdx.x;
-    int bh, qt;
-    if (CAUSAL && length_major) {
-        if (w_hw >= total) return;
-        const int nbh = total / num_qt;
-        bh = w_hw % nbh;
-        qt = num_qt - 1 - w_hw / nbh;
-    } else {
-        const int logical = (w_hw % NXCD) * per_xcd + w_hw / NXCD;
-        if (logical >= total) return;
-        bh = logical / num_qt;
-        qt = logical % num_qt;
-    }
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int h = lane >> 5;                         // half-wave
-    const int col = lane & 31;                       // query slot within a 32-row block
-
-    const int q0 = qt * T::BR;
-    const int qw0 = q0 + 32 * QB * wave;             // first query of this wave; block qb starts at qw0+32qb
-
-    const uint16_t* qh = static_cast<const uint16_t*>(a.q) + (size_t)bh * a.q_head_stride;
-    const uint16_t* kh = static_cast<const uint16_t*>(a.k) + (size_t)bh * a.kv_head_stride;
-    const uint16_t* vh = static_cast<const uint16_t*>(a.v) + (size_t)bh * a.kv_head_stride;
-
-    // keys this workgroup needs: [0, kv_end)
-    const int q_last = min(q0 + T::BR, a.n_q) - 1;
-    int kv_end = a.n_kv;
-    if (CAUSAL) kv_end = max(0, min(a.n_kv, q_last + a.offset + 1));
-    const int ntiles = (kv_end + T::BC - 1) / T::BC;
-
-    // per-wave visibility bounds (wave-uniform)
-    const int qw_last = min(qw0 + 32 * QB - 1, a.n_q - 1);
-    const int wave_key_end = qw0 >= a.n_q ? 0 : CAUSAL ? min(kv_end, qw_last + a.offset + 1) : kv_end;
-    const int wave_full_end = CAUSAL ? min(a.n_kv, qw0 + a.offset + 1) : a.n_kv;   // keys < this: all visible
-
-    // ---- global -> LDS loads.  Each tile gets buffer resources whose base is the tile's first key and whose
-    // bound is the rest of this head's key range, so loads past the last key return zeros; the whole
-    // offset is in the per-lane VGPR offset (the scalar offset stays 0).
-    const long long kv_bytes = (long long)a.n_kv * T::ROW;
-    // this wave fills segments wave, wave+NW, ...; lane L writes row RPS*seg + L/LPR, physical chunk L%LPR.
-    // Rows of segment wave+NW*k are those of segment `wave` plus NW*RPS*k (= 4096*k bytes), and the
-    // swizzles only look at row bits that this shift leaves alone.
-    int k_voff, v_voff;
-    {
-        const int r0 = T::RPS * wave + lane / T::LPR;
-        const int p = lane % T::LPR;
-        k_voff = r0 * T::ROW + 16 * (p ^ k_swz<D>(r0));
-        v_voff = r0 * T::ROW + 16 * (p ^ v_swz<D>(r0));
-    }
-    auto issue_tile = [&](int t) {
-        lds_char* kbuf = lds + (t % T::NK) * T::TILE;
-        lds_char* vbuf = lds + (T::NK + t % T::NV) * T::TILE;
-        const long long base = (long long)t * T::TILE;
-        const int left = (int)(kv_bytes - base);
-        const __amdgpu_buffer_rsrc_t krs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)kh + base), (short)0, left, BUF_RSRC_WORD3);
-        const __amdgpu_buffer_rsrc_t vrs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)vh + base), (short)0, left, BUF_RSRC_WORD3);
-#pragma unroll
-        for (int k = 0; k < T::SEGS_PER_WAVE; ++k) {
-            const int seg = wave + T::NW * k;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kbuf + seg * 1024), 16, k_voff, 4096 * k, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vbuf + seg * 1024), 16, v_voff, 4096 * k, 0, 0);
-        }
-    };
-
-    // ---- Q^T fragments (B operand): query qw0+32qb+col, head-dim elements 16*ks + 8*h .. +7.
-    // A negative scale negates Q (exact in bf16) so that every exponent is taken against a running max;
-    // a zero scale zeroes Q, which gives the same all-zero logits without multiplying -inf by zero.
-    const float scale_abs = fabsf(a.scale);
-    const unsigned neg = a.scale < 0.f ? 0x80008000u : 0u;
-    const unsigned keep = a.scale == 0.f ? 0u : 0xffffffffu;
-    bf16x8 qf[QB][T::NKS];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int qi = qw0 + 32 * qb + col;
-#pragma unroll
-        for (int ks = 0; ks < T::NKS; ++ks) {
-            u32x4 x = qi < a.n_q ? *reinterpret_cast<const u32x4*>(qh + (size_t)qi * D + 16 * ks + 8 * h)
-                                 : u32x4{0, 0, 0, 0};
-            x = (x ^ neg) & keep;
-            qf[qb][ks] = as_bf16x8(x);
-        }
-    }
-    const float c = a.scale == 0.f ? LOG2E : scale_abs * LOG2E;   // scale * log2(e), always > 0
-
-    // ---- per-lane LDS read offsets (the tile buffer and (kb, ks) parts are added as immediates)
-    const int kslot = swap23(col);                   // K row (within a 32-key block) feeding A-row `col`
-    int k_roff[T::NKS];
-#pragma unroll
-    for (int ks = 0; ks < T::NKS; ++ks) k_roff[ks] = kslot * T::ROW + 16 * ((2 * ks + h) ^ k_swz<D>(kslot));
-    // transpose reads: block b = lane/16 -> half-wave h and head-dim half dp; e = key within a group of
-    // four, s4 = which 4 head-dim values of the 16
-    int v_roff[T::NDB];
-    {
-        const int b = lane >> 4, j = lane & 15, e = j >> 2, s4 = j & 3, dp = b & 1;
-#pragma unroll
-        for (int db = 0; db < T::NDB; ++db) {
-            const int chunk = 4 * db + 2 * dp + (s4 >> 1);
-            v_roff[db] = (8 * h + e) * T::ROW + 16 * (chunk ^ v_swz<D>(e)) + 8 * (s4 & 1);
-        }
-    }
-
-    f32x16 acc[QB][T::NDB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int db = 0; db < T::NDB; ++db) acc[qb][db] = f32x16{};
-    // exponent reference (running max of raw dot products, may lag), the denominator (fp32 sum of the
-    // weights, for lse) and the sum of the weights' bf16 roundings (the weights P.V accumulates, for O)
-    float m[QB], l[QB], lt[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        m[qb] = -INFINITY;
-        l[qb] = 0.f;      // this half-wave's keys only; the halves are added at the end
-        lt[qb] = 0.f;
-    }
-    u32x4 p_cur[QB][T::NKB][2];   // bf16 weights of the previous tile, consumed by its P.V one step later
-
-    // Tiles this wave computes: a prefix [0, wave_tiles) of the workgroup's ntiles (causal waves stop early).
-    const int wave_tiles = min(ntiles, (wave_key_end + T::BC - 1) / T::BC);
-
-    // One pipelined step at tile t: S(t) = K_t Q^T, the P.V product of tile t-1 (weights from the previous
-    // step), then the weights of tile t.  In program order the MFMAs of both products come first and the
-    // softmax last, all in one straight-line block: the softmax waits only for S(t) and then issues while
-    // the P.V MFMAs run.  An output rescale caused by tile t is applied at the start of the next step, i.e.
-    // after P.V(t-1) (old reference) and before P.V(t) (new reference).
-    //
-    // The exponent reference m is not recomputed from every tile: the weights exp2(s*c - m*c) are taken
-    // against the current reference, and only if no reference exists yet or some weight sum exceeds 2^64
-    // (a score more than 64 exp2-units above the reference) is the tile redone against its true max.  Every
-    // weight is then below 2^64 and the accumulated sums stay far inside fp32 range, so the result equals
-    // the running-max formulation up to rounding; the row max drops out of the common path.
-    float alpha_prev[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) alpha_prev[qb] = 1.f;
-    bool moved_prev = false;
-    auto step = [&](auto do_s, auto do_pv, auto masked_c, int t, const lds_char* __restrict__ kbuf,
-                    const lds_char* __restrict__ vbuf) {
-        constexpr bool DO_S = decltype(do_s)::value, DO_PV = decltype(do_pv)::value;
-        constexpr bool MASKED = decltype(masked_c)::value;
-        // Per-lane LDS offsets pass through an empty statement here, so that the compiler forms
-        // "buffer + offset" once per step and folds the (kb, ks) constants into the instructions' offset
-        // fields, instead of hoisting every offset+constant combination out of the loop.
-#pragma unroll
-        for (int ks = 0; ks < T::NKS; ++ks) __asm__ volatile("" : "+v"(k_roff[ks]));
-#pragma unroll
-        for (int db = 0; db < T::NDB; ++db) __asm__ volatile("" : "+v"(v_roff[db]));
-        const int (&kro)[T::NKS] = k_roff;
-        const int (&vro)[T::NDB] = v_roff;
-        if (moved_prev) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                for (int db = 0; db < T::NDB; ++db) acc[qb][db] *= alpha_prev[qb];
-            moved_prev = false;
-        }
-        f32x16 s[QB][T::NKB];
-        if constexpr (DO_S) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                for (int kb = 0; kb < T::NKB; ++kb) s[qb][kb] = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < T::NKS; ++ks) {
-#pragma unroll
-                for (int kb = 0; kb < T::NKB; ++kb) {
-                    const u32x4 kv = *(const lds_u32x4*)(kbuf + kro[ks] + 32 * kb * T::ROW);
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb)
-                        s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qf[qb][ks], s[qb][kb], 0, 0, 0);
-                }
-            }
-        }
-        if constexpr (DO_PV) {   // O^T += V^T P^T for tile t-1; V^T operand by two transpose reads
-#pragma unroll
-            for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                    for (int db = 0; db < T::NDB; ++db) {
-                        const lds_char* p = vbuf + vro[db] + (32 * kb + 16 * ks) * T::ROW;
-                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * T::ROW));
-                        const u32x4 vv = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                                          __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
-#pragma unroll
-                        for (int qb = 0; qb < QB; ++qb)
-                            acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), as_bf16x8(p_cur[qb][kb][ks]),
-                                                                              acc[qb][db], 0, 0, 0);
-                    }
-        }
-        if constexpr (DO_S) {
-            if constexpr (MASKED) {   // keys past the end or in the causal future
-                const int kt = t * T::BC;
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    const int qi = qw0 + 32 * qb + col;
-                    const int lim = CAUSAL ? min(a.n_kv - 1, qi + a.offset) : a.n_kv - 1;   // last visible key
-#pragma unroll
-                    for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-                        for (int j = 0; j < 16; ++j) {
-                            const int key = kt + 32 * kb + 16 * (j >> 3) + 8 * h + (j & 7);
-                            if (key > lim) s[qb][kb][j] = -INFINITY;
-                        }
-                }
-            }
-            u32x4 p_next[QB][T::NKB][2];
-            float rs[QB], rt[QB];
-            // weights of tile t against reference m (m*c == mc; 0 stands in while no reference exists)
-            auto weights = [&](const float (&mc)[QB]) {
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    rs[qb] = 0.f;
-                    rt[qb] = 0.f;
-#pragma unroll
-                    for (int kb = 0; kb < T::NKB; ++kb) {
-                        float e[16];
-#pragma unroll
-                        for (int j = 0; j < 16; ++j) e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][j], c, -mc[qb]));
-                        float r8[8];   // pairwise row sum (short dependency chains)
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) r8[j] = e[2 * j] + e[2 * j + 1];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) r8[j] = r8[2 * j] + r8[2 * j + 1];
-                        rs[qb] += (r8[0] + r8[1]) + (r8[2] + r8[3]);
-#pragma unroll
-                        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                            for (int w = 0; w < 4; ++w) {
-                                p_next[qb][kb][ks][w] = pack_bf16(e[8 * ks + 2 * w], e[8 * ks + 2 * w + 1]);
-                                rt[qb] = add_bf16_pair(p_next[qb][kb][ks][w], rt[qb]);
-                            }
-                    }
-                }
-            };
-            float mc[QB];
-            bool redo = false;
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                mc[qb] = m[qb] == -INFINITY ? 0.f : m[qb] * c;
-                redo = redo || m[qb] == -INFINITY;
-            }
-            weights(mc);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) redo = redo || !(rs[qb] <= REF_BOUND);
-            float alpha[QB];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) alpha[qb] = 1.f;
-            if (__any(redo)) {
-                // rare: the first visible keys, or a score far above the reference.  Move the reference to
-                // the running max (for every row of the wave) and recompute the weights.
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    float mt = -INFINITY;
-#pragma unroll
-                    for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-                        for (int j = 0; j < 16; ++j) mt = fmaxf(mt, s[qb][kb][j]);
-                    mt = fmaxf(mt, wave_xor32(mt));
-                    const float m_new = fmaxf(m[qb], mt);
-                    alpha[qb] = m[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m[qb] - m_new) * c);
-                    m[qb] = m_new;
-                    mc[qb] = m_new == -INFINITY ? 0.f : m_new * c;
-                    alpha_prev[qb] = alpha[qb];
-                }
-                moved_prev = true;
-                weights(mc);
-            }
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                l[qb] = __builtin_fmaf(l[qb], alpha[qb], rs[qb]);
-                lt[qb] = __builtin_fmaf(lt[qb], alpha[qb], rt[qb]);
-            }
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) p_cur[qb][kb][ks] = p_next[qb][kb][ks];
-        }
-    };
-    using yes = std::integral_constant<bool, true>;
-    using no = std::integral_constant<bool, false>;
-
-    // prologue: tiles 0 .. L-1 in flight, tile 0 must have landed (in every wave) before the first step
-    for (int t0 = 0; t0 < T::L && t0 < ntiles; ++t0) issue_tile(t0);
-    if (ntiles >= T::L) __builtin_amdgcn_s_waitcnt(0x0F70 | ((T::L - 1) * T::LPT));
-    else __builtin_amdgcn_s_waitcnt(0x0F70);
-    lds_barrier();
-
-    // End of iteration t: this wave's loads of tile t+1 have landed (tiles t+2 .. t+L-1 may still fly) and,
-    // after the barrier, every wave's have, and every wave is done with K_t and V_{t-1}; tile t+L is then
-    // loaded into their buffers.  All waves run exactly ntiles such barriers, whether or not they still have
-    // tiles to compute.
-    auto retire = [&](int t) {
-        if (t + T::L - 1 < ntiles) __builtin_amdgcn_s_waitcnt(0x0F70 | ((T::L - 2) * T::LPT));
-        else __builtin_amdgcn_s_waitcnt(0x0F70);
-        lds_barrier();
-        if (t + T::L < ntiles) issue_tile(t + T::L);
-    };
-    auto kbuf_of = [&](int t) { return (const lds_char*)(lds + (t % T::NK) * T::TILE); };
-    auto vbuf_of = [&](int t) { return (const lds_char*)(lds + (T::NK + t % T::NV) * T::TILE); };
-    // The steady-state iteration gets its buffers as restrict-qualified pointers, distinct from those the
-    // loads issued by retire() write (tile t+L), so the compiler does not wait for those loads before
-    // reading tile t and t-1 (the explicit vmcnt wait before every barrier is what makes that true).
-    auto iterate = [&](int t, const lds_char* __restrict__ kb, const lds_char* __restrict__ vb) {
-        step(yes{}, yes{}, no{}, t, kb, vb);
-        retire(t);
-    };
-    // Tiles [0, full_tiles) of this wave need no mask; [full_tiles, wave_tiles) are the diagonal or ragged ones.
-    const int full_tiles = min(wave_tiles, wave_full_end / T::BC);
-    auto iterate_masked = [&](int t, const lds_char* __restrict__ kb, const lds_char* __restrict__ vb) {
-        step(yes{}, yes{}, yes{}, t, kb, vb);
-        retire(t);
-    };
-    int t = 0;
-    if (ntiles > 0) {
-        if (wave_tiles > 0) {
-            if (full_tiles > 0) step(yes{}, no{}, no{}, 0, kbuf_of(0), vbuf_of(T::NV - 1));
-            else step(yes{}, no{}, yes{}, 0, kbuf_of(0), vbuf_of(T::NV - 1));
-        }
-        retire(0);
-        for (t = 1; t < full_tiles; ++t) iterate(t, kbuf_of(t), vbuf_of(t - 1));
-        for (t = max(t, 1); t < wave_tiles; ++t) iterate_masked(t, kbuf_of(t), vbuf_of(t - 1));
-        if (wave_tiles > 0) step(no{}, yes{}, no{}, t, kbuf_of(t), vbuf_of(t - 1));   // P.V of the last tile
-        for (t = max(t, 1); t < ntiles; ++t) retire(t);
-    }
-
-    // ---- epilogue: one division by the final denominator; lse = scaled reference + ln(l)
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int qi = qw0 + 32 * qb + col;
-        const float l_tot = l[qb] + wave_xor32(l[qb]);
-        const float lt_tot = lt[qb] + wave_xor32(lt[qb]);
-        if (qi < a.n_q) store_row<T::NDB, OUT_F32>(a, bh, qi, h, acc[qb], l_tot, lt_tot, m[qb], scale_abs);
-    }
-}
-
 // LDS above the default limit needs an explicit opt-in, once per kernel and device.  Threads that race on
 // the first launch may both set the attribute, which is harmless; the flags themselves are atomic.
 template <auto KERN>
@@ -584,30 +148,13 @@ hipError_t allow_lds(int bytes) {
     return hipSuccess;
 }
 
-template <int D, bool CAUSAL, bool OUT_F32>
-hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
-    using T = Tile<D>;
-    const int num_qt = (a.n_q + T::BR - 1) / T::BR;
-    const long long total_ll = (long long)num_qt * a.bh;
-    if (total_ll > 0x7fffffffLL - NXCD) return hipErrorInvalidValue;
-    if ((long long)a.n_kv * T::ROW > 0x7fffffffLL) return hipErrorInvalidValue;   // buffer bound is 31-bit
-    const int total = (int)total_ll;
-    const int per_xcd = (total + NXCD - 1) / NXCD;
-    const int grid = per_xcd * NXCD;
-    const int length_major = CAUSAL && (long long)a.offset < (long long)a.n_kv - 1;
-    auto kern = fwd_bf16_kernel<D, CAUSAL, OUT_F32>;
-    if (hipError_t e = allow_lds<fwd_bf16_kernel<D, CAUSAL, OUT_F32>>(T::LDS); e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(T::THREADS), T::LDS, s, a, num_qt, total, per_xcd, length_major);
-    return hipGetLastError();
-}
-
-// ---- d = 128: three-stage software pipeline with a fixed interleave.
+// ---- Three-stage software pipeline with a fixed interleave (d = 64 and d = 128).
 //
 // Step t of a wave computes the softmax of tile t, whose scores S(t) were produced by the previous step,
 // next to two batches of MFMAs that do not depend on it:
-//   part 1:  P.V of tile t-1 (16 MFMAs, V^T by transpose reads)      with the scaling and exp of tile t's scores
-//   part 2:  S(t+1) = K_{t+1} Q^T (16 MFMAs)                          with the row sums and bf16 packs of tile t
-// so every VALU instruction of a step has an MFMA of the same step to hide under, and the order (two MFMAs,
+//   part 1:  P.V of tile t-1 (d/8 MFMAs, V^T by transpose reads)     with the scaling and exp of tile t's scores
+//   part 2:  S(t+1) = K_{t+1} Q^T (d/8 MFMAs)                        with the row sums and bf16 packs of tile t
+// so every VALU instruction of a step has an MFMA of the same step to hide under, and the order (MFMAs,
 // a share of the VALU work, the LDS reads for two MFMAs ahead) is pinned with scheduling fences.  Scores
 // and weights need no double buffers: part 1 reads the scores before part 2 overwrites them, and part 2
 // writes the new weights after part 1's MFMAs have read the old ones.  The rare redo of a tile (see the
@@ -618,10 +165,17 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
 // eight waves V_{t+1} is waited for at the end of step t, one step before its P.V, so that each step can
 // read the next step's first two V^T operands before its barrier and the next P.V starts without waiting
 // for LDS.
-template <int NW_>
+template <int NW_, int D_>
 struct P3 {
-    static constexpr int D = 128, NW = NW_, THREADS = 64 * NW, BR = 32 * NW, BC = 64;
+    static constexpr int D = D_, NW = NW_, THREADS = 64 * NW, BR = 32 * NW, BC = 64;
     static constexpr int NKB = BC / 32, NDB = D / 32, NKS = D / 16, ROW = 2 * D, TILE = BC * ROW;
+    // MFMAs of a step's two parts: P.V(t-1) (NKB 32-key blocks x 2 k-steps x NDB head-dim blocks) and
+    // S(t+1) (NKS k-steps x NKB key blocks); the tile's 32 scores per lane spread evenly over them
+    static constexpr int NPV = NKB * 2 * NDB, NS = NKS * NKB;
+    static constexpr int EXP_PER_PV = 16 * NKB / NPV, PAIRS_PER_S = 8 * NKB / NS;
+    // d = 64 divides O by the fp32 sum of the weights' bf16 roundings (a second denominator, one dot2 per
+    // weight pair); d = 128 by the fp32 sum of the weights
+    static constexpr bool LT = D == 64;
     static constexpr int SEGS = TILE / 1024, SEGS_PER_WAVE = SEGS / NW;
     static constexpr int RPS = 1024 / ROW, LPR = ROW / 16;
     // K and V buffers: K_j is loaded NK-2 steps and V_j NV-1 steps before its first use
@@ -639,15 +193,17 @@ struct P3 {
     static constexpr int AFTER = (DK < DV ? 1 + 2 * (DK - 1) : 2 * (DV - 1)) * SEGS_PER_WAVE;
     static constexpr int LEAD = NK > NV - 1 ? NK : NV - 1;   // all loads up to retire(t-1) exist iff t-1+LEAD < ntiles
     static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
+    static_assert(D == 64 || D == 128, "head dimension 64 or 128");
+    static_assert(EXP_PER_PV * NPV == 16 * NKB && PAIRS_PER_S * NS == 8 * NKB, "scores spread evenly");
     static_assert(NK + NV + EXTRA >= NW + 1, "the epilogue stages every wave's rows in its own free buffer");
     static_assert((NK - 1) * TILE + 32 * ROW < 65536 && (NV - 1) * TILE + 52 * ROW < 65536,
                   "constant buffer bases fit the LDS reads' 16-bit offset field");
 };
 
-template <int NW, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, int num_qt, int total, int per_xcd,
-                                                                    int length_major) {
-    using T = P3<NW>;
+template <int NW, int D_, bool CAUSAL, bool OUT_F32>
+__global__ __launch_bounds__((P3<NW, D_>::THREADS), 2) void fwd_p3_kernel(FwdArgs a, int num_qt, int total,
+                                                                        int per_xcd, int length_major) {
+    using T = P3<NW, D_>;
     constexpr int D = T::D;
     constexpr int WS = T::WSTRIDE;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -779,6 +335,7 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
 #pragma unroll
     for (int db = 0; db < T::NDB; ++db) acc[db] = f32x16{};
     float m = -INFINITY, l = 0.f, alpha_prev = 1.f;
+    [[maybe_unused]] float lt = 0.f;   // sum of the weights' bf16 roundings (the values P.V accumulates)
     bool moved = false;
     f32x16 s[T::NKB];           // scores of the tile whose softmax is next
     u32x4 p[T::NKB][2];         // bf16 weights of the tile whose P.V is next
@@ -815,9 +372,10 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
                 sc[kb][j] = __builtin_bit_cast(float, (b & ~msk) | (0xff800000u & msk));
             }
     };
-    // weights and their row sum against reference mc (the plain form, used by the rare redo)
-    auto weights = [&](const f32x16 (&sc)[T::NKB], float mc) __attribute__((always_inline)) {
+    // weights and their row sums against reference mc (the plain form, used by the rare redo)
+    auto weights = [&](const f32x16 (&sc)[T::NKB], float mc, float& rt) __attribute__((always_inline)) {
         float rs = 0.f;
+        rt = 0.f;
 #pragma unroll
         for (int kb = 0; kb < T::NKB; ++kb) {
             float e[16];
@@ -832,7 +390,10 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int w = 0; w < 4; ++w) p[kb][ks][w] = pack_bf16(e[8 * ks + 2 * w], e[8 * ks + 2 * w + 1]);
+                for (int w = 0; w < 4; ++w) {
+                    p[kb][ks][w] = pack_bf16(e[8 * ks + 2 * w], e[8 * ks + 2 * w + 1]);
+                    if constexpr (T::LT) rt = add_bf16_pair(p[kb][ks][w], rt);
+                }
         }
         return rs;
     };
@@ -863,9 +424,9 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
         }
         const float mc = mcr;
         float e[2 * 16];
-        u32x4 kv[16];
+        u32x4 kv[T::NS];
         auto kread = [&](int i) __attribute__((always_inline)) {
-            kv[i] = *(const lds_u32x4*)(kn + k_roff[i >> 1] + 32 * (i & 1) * T::ROW);
+            kv[i] = *(const lds_u32x4*)(kn + k_roff[i / T::NKB] + 32 * (i % T::NKB) * T::ROW);
         };
         // ---- part 1: P.V(t-1) (two transpose reads per MFMA, two MFMAs ahead) with the exps of tile t.
         // The wave runs part 1, which carries most of the step's VALU work, at raised priority and part 2 at the
@@ -874,9 +435,9 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
         // raising part 2 instead, or one wave of each pair throughout, measured -0.1 and +-0 %).
         __builtin_amdgcn_s_setprio(1);
         {
-            i16x4 vl[16], vhh[16];
+            i16x4 vl[T::NPV], vhh[T::NPV];
             auto vread = [&](int i) __attribute__((always_inline)) {
-                const int kb = i >> 3, ks = (i >> 2) & 1, db = i & 3;
+                const int kb = i / (2 * T::NDB), ks = (i / T::NDB) & 1, db = i % T::NDB;
                 const lds_char* q = vp + v_roff[db] + (32 * kb + 16 * ks) * T::ROW;
                 vl[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)q);
                 vhh[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q + 4 * T::ROW));
@@ -894,20 +455,21 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < T::NPV; ++i) {
                 if constexpr (PV) {
-                    if (i + 2 < 16) vread(i + 2);
-                    const int kb = i >> 3, ks = (i >> 2) & 1, db = i & 3;
+                    if (i + 2 < T::NPV) vread(i + 2);
+                    const int kb = i / (2 * T::NDB), ks = (i / T::NDB) & 1, db = i % T::NDB;
                     const u32x4 vv = {__builtin_bit_cast(u32x2, vl[i])[0], __builtin_bit_cast(u32x2, vl[i])[1],
                                       __builtin_bit_cast(u32x2, vhh[i])[0], __builtin_bit_cast(u32x2, vhh[i])[1]};
                     acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), as_bf16x8(p[kb][ks]), acc[db], 0, 0, 0);
                 }
                 if constexpr (SOFT) {
-                    e[2 * i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i >> 3][(2 * i) & 15], c, -mc));
-                    e[2 * i + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i >> 3][(2 * i + 1) & 15], c, -mc));
+#pragma unroll
+                    for (int x = T::EXP_PER_PV * i; x < T::EXP_PER_PV * (i + 1); ++x)
+                        e[x] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[x >> 4][x & 15], c, -mc));
                 }
                 if constexpr (S && PV) {
-                    if (i >= 14) kread(i - 14);   // the first K operands of part 2, under the last P.V MFMAs
+                    if (i >= T::NPV - 2) kread(i - (T::NPV - 2));   // the first K operands of part 2, under the last P.V MFMAs
                 }
                 if constexpr (PV) __builtin_amdgcn_sched_barrier(0);
             }
@@ -915,6 +477,7 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
         // ---- part 2: S(t+1) (one K read per MFMA, two MFMAs ahead) with the sums and packs of tile t
         __builtin_amdgcn_s_setprio(0);
         float rs = 0.f;   // the tile's weight sum, accumulated pair by pair under the S MFMAs
+        [[maybe_unused]] float rt = 0.f;   // and the sum of their bf16 roundings
         {
             if constexpr (S && !PV) {
                 kread(0);
@@ -922,17 +485,21 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < T::NS; ++i) {
                 if constexpr (S) {
-                    if (i + 2 < 16) kread(i + 2);
-                    const int ks = i >> 1, kb = i & 1;
+                    if (i + 2 < T::NS) kread(i + 2);
+                    const int ks = i / T::NKB, kb = i % T::NKB;
                     s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv[i]), qf[ks], ks == 0 ? f32x16{} : s[kb], 0, 0, 0);
                 }
                 if constexpr (SOFT) {
-                    const float pair = e[2 * i] + e[2 * i + 1];
-                    rs = i == 0 ? pair : rs + pair;
-                    p[i >> 3][(i >> 2) & 1][i & 3] = pack_bf16(e[2 * i], e[2 * i + 1]);
-                    __asm__ volatile("" ::"v"(p[i >> 3][(i >> 2) & 1][i & 3]));   // keep the pack in this slot
+#pragma unroll
+                    for (int y = T::PAIRS_PER_S * i; y < T::PAIRS_PER_S * (i + 1); ++y) {
+                        const float pair = e[2 * y] + e[2 * y + 1];
+                        rs = y == 0 ? pair : rs + pair;
+                        p[y >> 3][(y >> 2) & 1][y & 3] = pack_bf16(e[2 * y], e[2 * y + 1]);
+                        __asm__ volatile("" ::"v"(p[y >> 3][(y >> 2) & 1][y & 3]));   // keep the pack in this slot
+                        if constexpr (T::LT) rt = add_bf16_pair(p[y >> 3][(y >> 2) & 1][y & 3], rt);
+                    }
                 }
                 if constexpr (S) __builtin_amdgcn_sched_barrier(0);
             }
@@ -965,9 +532,10 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
                 m = m_new;
                 mcr = m_new == -INFINITY ? 0.f : m_new * c;
                 bnd = m_new == -INFINITY ? -1.f : REF_BOUND;
-                rs = weights(sc, mcr);
+                rs = weights(sc, mcr, rt);
             }
             l = __builtin_fmaf(l, alpha, rs);
+            if constexpr (T::LT) lt = __builtin_fmaf(lt, alpha, rt);
         }
         if constexpr (SOFT && T::VAHEAD) {
             // the next step's first two V^T operands (V_t, landed by the previous retire), under this barrier
@@ -1012,18 +580,21 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
     // The wave's 32 rows of the running partial (when there is one) and of the output are addressed through
     // buffer resources bounded at the last query row: loads past it return zeros and stores are dropped.
     const int rows_left = __builtin_amdgcn_readfirstlane(max(0, min(32, a.n_q - qw0)));   // uniform, kept scalar
+    // Output rows move in 16-byte pieces: PPR pieces of four floats per fp32 row (RPI rows per wave
+    // instruction), BPPR pieces of eight bf16 per bf16 row (BRPI rows per instruction).
+    constexpr int PPR = D / 4, RPI = 64 / PPR, BPPR = D / 8, BRPI = 64 / BPPR;
     // The running partial, in the order the epilogue writes: with fp32 output lane l holds floats
-    // 4*(l%32)..+3 of row 2k + l/32 in prev[k]; with bf16 output floats 8*(l%16) + 4*(k%2)..+3 of row
-    // 4*(k/2) + l/16.
-    f32x4 prev[16];
+    // 4*(l%PPR)..+3 of row RPI*k + l/PPR in prev[k]; with bf16 output floats 8*(l%BPPR) + 4*(k%2)..+3 of
+    // row BRPI*(k/2) + l/BPPR.  Either way D/8 pieces per lane.
+    f32x4 prev[D / 8];
     float lse_pv = -INFINITY;   // lse of the partial for row qw0 + col
     auto fetch_prev = [&]() __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(a.o_prev + (size_t)bh * a.q_head_stride + (size_t)qw0 * D), (short)0, rows_left * D * 4, BUF_RSRC_WORD3);
-        const int voff = OUT_F32 ? (lane >> 5) * D * 4 + 16 * (lane & 31) : (lane >> 4) * D * 4 + 32 * (lane & 15);
+        const int voff = OUT_F32 ? (lane / PPR) * D * 4 + 16 * (lane % PPR) : (lane / BPPR) * D * 4 + 32 * (lane % BPPR);
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int koff = OUT_F32 ? 2 * k * D * 4 : 4 * (k >> 1) * D * 4 + 16 * (k & 1);
+        for (int k = 0; k < D / 8; ++k) {
+            const int koff = OUT_F32 ? RPI * k * D * 4 : BRPI * (k >> 1) * D * 4 + 16 * (k & 1);
             prev[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, koff, 0));
         }
         if (col < rows_left) lse_pv = a.lse_prev[(size_t)bh * a.n_q + qw0 + col];
@@ -1097,6 +668,10 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
         const float l_tot = l + wave_xor32(l);
         const float lb = l_tot > 0.f ? m * scale_abs + logf(l_tot) : -INFINITY;
         float cb = l_tot > 0.f ? 1.f / l_tot : 0.f;   // factor on this launch's accumulator
+        if constexpr (T::LT) {
+            const float lt_tot = lt + wave_xor32(lt);
+            cb = l_tot > 0.f && lt_tot > 0.f ? 1.f / lt_tot : 0.f;
+        }
         float ca = 0.f;                               // factor on the running partial
         float lse = lb;
         if (a.o_prev) {
@@ -1113,12 +688,15 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
             }
         }
         if (h == 0 && col < rows_left) a.lse[(size_t)bh * a.n_q + qi] = lse;
-        // A free 16 KiB LDS buffer per wave: after the last barrier only the V buffer of the last tile may
-        // still be read (by waves finishing their last P.V); nothing else is read or loaded any more.
+        // A free tile buffer per wave (32 fp32 rows fill one): after the last barrier only the V buffer of the
+        // last tile may still be read (by waves finishing their last P.V); nothing else is read or loaded.
+        static_assert(32 * D * 4 == T::TILE, "a wave's fp32 rows fill one tile buffer");
         const int busy = ntiles > 0 ? T::NK + (ntiles - 1) % T::NV : T::NK + T::NV;
         const int slot = wave < busy ? wave : wave + 1;
         lds_char* const st = lds + slot * T::TILE;
-        // row r, 16-byte piece q at piece q ^ r of the row (conflict-free writes and reads)
+        // row r, 16-byte piece q at piece q ^ (r mod PPR) of the row (conflict-free writes and reads); every
+        // r here is below 32, so with 32 pieces per row the reduction is left out
+        auto pswz = [](int r) __attribute__((always_inline)) { return PPR == 32 ? r : r % PPR; };
 #pragma unroll
         for (int db = 0; db < T::NDB; ++db)
 #pragma unroll
@@ -1126,7 +704,7 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
                 const int q = 8 * db + 2 * g + h;
                 const f32x4 o4 = {acc[db][4 * g] * cb, acc[db][4 * g + 1] * cb, acc[db][4 * g + 2] * cb,
                                   acc[db][4 * g + 3] * cb};
-                *(lds_f32x4*)(st + col * 512 + 16 * (q ^ col)) = o4;
+                *(lds_f32x4*)(st + col * (D * 4) + 16 * (q ^ pswz(col))) = o4;
             }
         __asm__ volatile("" ::: "memory");   // the reads below see this wave's writes (LDS keeps a wave's order)
         const int ca_bits = __builtin_bit_cast(int, ca);
@@ -1134,58 +712,58 @@ __global__ __launch_bounds__(P3<NW>::THREADS, 2) void fwd_p3_kernel(FwdArgs a, i
         if constexpr (OUT_F32) {
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)(static_cast<float*>(a.o) + obase), (short)0, rows_left * D * 4, BUF_RSRC_WORD3);
-            const int q = lane & 31;
-            f32x4 o4[16];
+            const int q = lane % PPR;
+            f32x4 o4[32 / RPI];
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const int r = 2 * k + (lane >> 5);
-                o4[k] = *(const lds_f32x4*)(st + r * 512 + 16 * (q ^ r));
+            for (int k = 0; k < 32 / RPI; ++k) {
+                const int r = RPI * k + lane / PPR;
+                o4[k] = *(const lds_f32x4*)(st + r * (D * 4) + 16 * (q ^ pswz(r)));
             }
             if (a.o_prev) {
 #pragma unroll
-                for (int k = 0; k < 16; ++k) {
-                    const int r = 2 * k + (lane >> 5);
+                for (int k = 0; k < 32 / RPI; ++k) {
+                    const int r = RPI * k + lane / PPR;
                     o4[k] += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * r, ca_bits)) * prev[k];
                 }
             }
-            const int voff = (lane >> 5) * D * 4 + 16 * q;
+            const int voff = (lane / PPR) * D * 4 + 16 * q;
 #pragma unroll
-            for (int k = 0; k < 16; ++k)
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o4[k]), rs, voff, 2 * k * D * 4, 0);
+            for (int k = 0; k < 32 / RPI; ++k)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o4[k]), rs, voff, RPI * k * D * 4, 0);
         } else {
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)(static_cast<uint16_t*>(a.o) + obase), (short)0, rows_left * D * 2, BUF_RSRC_WORD3);
-            const int q = lane & 15;
-            f32x4 lo[8], hi[8];
+            const int q = lane % BPPR;
+            f32x4 lo[32 / BRPI], hi[32 / BRPI];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int r = 4 * k + (lane >> 4);
-                lo[k] = *(const lds_f32x4*)(st + r * 512 + 16 * ((2 * q) ^ r));
-                hi[k] = *(const lds_f32x4*)(st + r * 512 + 16 * ((2 * q + 1) ^ r));
+            for (int k = 0; k < 32 / BRPI; ++k) {
+                const int r = BRPI * k + lane / BPPR;
+                lo[k] = *(const lds_f32x4*)(st + r * (D * 4) + 16 * ((2 * q) ^ pswz(r)));
+                hi[k] = *(const lds_f32x4*)(st + r * (D * 4) + 16 * ((2 * q + 1) ^ pswz(r)));
             }
             if (a.o_prev) {
 #pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int r = 4 * k + (lane >> 4);
+                for (int k = 0; k < 32 / BRPI; ++k) {
+                    const int r = BRPI * k + lane / BPPR;
                     const float car = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * r, ca_bits));
                     lo[k] += car * prev[2 * k];
                     hi[k] += car * prev[2 * k + 1];
                 }
             }
-            const int voff = (lane >> 4) * D * 2 + 16 * q;
+            const int voff = (lane / BPPR) * D * 2 + 16 * q;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < 32 / BRPI; ++k) {
                 const u32x4 o4 = {pack_bf16(lo[k][0], lo[k][1]), pack_bf16(lo[k][2], lo[k][3]),
                                   pack_bf16(hi[k][0], hi[k][1]), pack_bf16(hi[k][2], hi[k][3])};
-                __builtin_amdgcn_raw_buffer_store_b128(o4, rs, voff, 4 * k * D * 2, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(o4, rs, voff, BRPI * k * D * 2, 0);
             }
         }
     }
 }
 
-template <int NW, bool CAUSAL, bool OUT_F32>
+template <int NW, int D, bool CAUSAL, bool OUT_F32>
 hipError_t launch_p3(const FwdArgs& a, hipStream_t st) {
-    using T = P3<NW>;
+    using T = P3<NW, D>;
     const int num_qt = (a.n_q + T::BR - 1) / T::BR;
     const long long total_ll = (long long)num_qt * a.bh;
     if (total_ll > 0x7fffffffLL - NXCD) return hipErrorInvalidValue;
@@ -1195,23 +773,23 @@ hipError_t launch_p3(const FwdArgs& a, hipStream_t st) {
     const int grid = per_xcd * NXCD;
     // query tiles differ in length when some row does not see every key (row 0 sees keys up to 0 + offset)
     const int length_major = CAUSAL && (long long)a.offset < (long long)a.n_kv - 1;
-    auto kern = fwd_p3_kernel<NW, CAUSAL, OUT_F32>;
-    if (hipError_t e = allow_lds<fwd_p3_kernel<NW, CAUSAL, OUT_F32>>(T::LDS); e != hipSuccess) return e;
+    auto kern = fwd_p3_kernel<NW, D, CAUSAL, OUT_F32>;
+    if (hipError_t e = allow_lds<fwd_p3_kernel<NW, D, CAUSAL, OUT_F32>>(T::LDS); e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(T::THREADS), T::LDS, st, a, num_qt, total, per_xcd, length_major);
     return hipGetLastError();
 }
 
 }  // namespace
 
-// Workgroup size of the d = 128 kernel.  Eight waves (256 query rows, one workgroup per CU: both waves of a
+// Workgroup size of the bf16 kernel.  Eight waves (256 query rows, one workgroup per CU: both waves of a
 // SIMD share each K/V tile) unless the launch has fewer such tiles than CUs, or its rows are short and causal
 // (fewer than 3072 keys), where 128-row workgroups fill the chip and balance the diagonal better.  Measured
-// against four waves with the length-major order of causal launches: +4 to +14 % on causal rows of 3072 to
-// 8192 keys, +2 to +6 % without a mask from 1 to 8 tiles per CU, -4 to -6 % on causal rows of 1024 and
-// 2048 keys at 4 tiles per CU.  ATTN_BF16_D128_WAVES=4 or 8 forces one of them (used by the tests to run
-// every shape through both).
-static int d128_waves(const FwdArgs& a) {
-    if (const char* e = getenv("ATTN_BF16_D128_WAVES")) {
+// at d = 128 against four waves with the length-major order of causal launches: +4 to +14 % on causal rows
+// of 3072 to 8192 keys, +2 to +6 % without a mask from 1 to 8 tiles per CU, -4 to -6 % on causal rows of 1024
+// and 2048 keys at 4 tiles per CU; at d = 64, +1.7 % on 16384 keys without a mask.  ATTN_BF16_D128_WAVES and
+// ATTN_BF16_D64_WAVES (4 or 8) force one of them (used by the tests to run every shape through both).
+static int bf16_waves(const FwdArgs& a) {
+    if (const char* e = getenv(a.d == 128 ? "ATTN_BF16_D128_WAVES" : "ATTN_BF16_D64_WAVES")) {
         const int v = atoi(e);
         if (v == 4 || v == 8) return v;
     }
@@ -1224,16 +802,20 @@ static int d128_waves(const FwdArgs& a) {
 hipError_t launch_fwd_bf16(const FwdArgs& a, bool out_f32, hipStream_t s) {
     const bool c = a.causal != 0;
     if (a.d == 128) {
-        if (d128_waves(a) == 8) {
-            if (c) return out_f32 ? launch_p3<8, true, true>(a, s) : launch_p3<8, true, false>(a, s);
-            return out_f32 ? launch_p3<8, false, true>(a, s) : launch_p3<8, false, false>(a, s);
+        if (bf16_waves(a) == 8) {
+            if (c) return out_f32 ? launch_p3<8, 128, true, true>(a, s) : launch_p3<8, 128, true, false>(a, s);
+            return out_f32 ? launch_p3<8, 128, false, true>(a, s) : launch_p3<8, 128, false, false>(a, s);
         }
-        if (c) return out_f32 ? launch_p3<4, true, true>(a, s) : launch_p3<4, true, false>(a, s);
-        return out_f32 ? launch_p3<4, false, true>(a, s) : launch_p3<4, false, false>(a, s);
+        if (c) return out_f32 ? launch_p3<4, 128, true, true>(a, s) : launch_p3<4, 128, true, false>(a, s);
+        return out_f32 ? launch_p3<4, 128, false, true>(a, s) : launch_p3<4, 128, false, false>(a, s);
     }
     if (a.d == 64) {
-        if (c) return out_f32 ? launch_t<64, true, true>(a, s) : launch_t<64, true, false>(a, s);
-        return out_f32 ? launch_t<64, false, true>(a, s) : launch_t<64, false, false>(a, s);
+        if (bf16_waves(a) == 8) {
+            if (c) return out_f32 ? launch_p3<8, 64, true, true>(a, s) : launch_p3<8, 64, true, false>(a, s);
+            return out_f32 ? launch_p3<8, 64, false, true>(a, s) : launch_p3<8, 64, false, false>(a, s);
+        }
+        if (c) return out_f32 ? launch_p3<4, 64, true, true>(a, s) : launch_p3<4, 64, true, false>(a, s);
+        return out_f32 ? launch_p3<4, 64, false, true>(a, s) : launch_p3<4, 64, false, false>(a, s);
     }
     return hipErrorInvalidValue;
 }

@@ -409,6 +409,8 @@ def main():
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "profiles"))
     ap.add_argument("--raw", default=os.path.join(ROOT, "gpurun_out", "prof_raw"))
     a = ap.parse_args()
+    # the profiled children run from /tmp, so relative paths are taken against this directory here
+    a.out, a.raw = os.path.abspath(a.out), os.path.abspath(a.raw)
     os.makedirs(a.out, exist_ok=True)
     what = a.what.split(",")
     names = a.workloads.split(",")

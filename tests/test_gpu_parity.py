@@ -149,10 +149,11 @@ def test_small_full(i):
         assert_parity(err, w.dtype, f"{w.name} chunks={P}")
 
 
-# The bf16 d = 128 kernel runs as four-wave (128-row) or eight-wave (256-row) workgroups, chosen by the
-# launch size; ATTN_BF16_D128_WAVES forces one.  Every shape below runs through both, against the oracle, and
-# the two must agree bit for bit (each row sees the same tiles in the same order either way).
-D128_SHAPES = [
+# The bf16 kernel runs as four-wave (128-row) or eight-wave (256-row) workgroups, chosen by the launch size;
+# ATTN_BF16_D128_WAVES and ATTN_BF16_D64_WAVES force one.  Every shape below runs through both at both head
+# dimensions, against the oracle, and the two must agree bit for bit (each row sees the same tiles in the
+# same order either way).
+WG_SHAPES = [
     # B, H, N_q, N_kv, causal
     (1, 2, 300, 777, False),
     (1, 2, 300, 777, True),
@@ -167,15 +168,16 @@ D128_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("case", D128_SHAPES, ids=lambda c: "x".join(map(str, c[:4])) + ("c" if c[4] else "n"))
-def test_d128_both_workgroup_sizes(case, monkeypatch):
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("case", WG_SHAPES, ids=lambda c: "x".join(map(str, c[:4])) + ("c" if c[4] else "n"))
+def test_bf16_both_workgroup_sizes(case, d, monkeypatch):
     B, H, N_q, N_kv, causal = case
-    w = W.Workload("d128wg", B, H, N_q, N_kv, 128, "bf16", causal, 1, seed=3000 + N_q + N_kv)
+    w = W.Workload(f"d{d}wg", B, H, N_q, N_kv, d, "bf16", causal, 1, seed=3000 + N_q + N_kv + d)
     st, (q, k, v) = make(w)
     o_ref, l_ref = oracle_full(st, w)
     outs = {}
     for waves in ("4", "8"):
-        monkeypatch.setenv("ATTN_BF16_D128_WAVES", waves)
+        monkeypatch.setenv(f"ATTN_BF16_D{d}_WAVES", waves)
         o, lse = A.fwd(q, k, v, causal=causal, scale=w.scale)
         o32, l32 = A.fwd_ex(q, k, v, causal=causal, scale=w.scale, out_dtype=torch.float32)
         torch.cuda.synchronize()

@@ -5,8 +5,8 @@ single division; chunks folded as in the "ATTENTION2D" explainer, section 2).
 
 The cases are drawn once from a fixed seed, so the set is the same on every run.  Sizes stay where the
 oracle finishes in well under a second per case while still spanning several key tiles with ragged tails.
-For d = 128 in bf16 every case also fixes the workgroup size (four or eight waves) through
-ATTN_BF16_D128_WAVES, alternating, so that both d = 128 kernels meet shapes the launch heuristic would not
+For bf16 every case also fixes the workgroup size (four or eight waves) through ATTN_BF16_D128_WAVES or
+ATTN_BF16_D64_WAVES, alternating, so that both workgroup sizes meet shapes the launch heuristic would not
 hand them: query counts below one workgroup, key counts below one tile, causal launches whose rows see no key.
 """
 from __future__ import annotations
@@ -36,7 +36,7 @@ def _cases(n: int = 60):
         causal = bool(rng.integers(0, 2))
         q_std = float(rng.choice([1.0, 1.0, 3.0]))
         chunks = int(rng.choice([1, 1, 2, 5]))
-        waves = ("4" if i % 2 else "8") if (dt == "bf16" and d == 128) else None
+        waves = ("4" if i % 2 else "8") if dt == "bf16" else None
         out.append((B, H, N_q, N_kv, d, dt, causal, q_std, chunks, waves))
     return out
 
@@ -61,7 +61,7 @@ def _gpu():
 def test_random_shape(case, monkeypatch):
     B, H, N_q, N_kv, d, dt, causal, q_std, chunks, waves = case
     if waves:
-        monkeypatch.setenv("ATTN_BF16_D128_WAVES", waves)
+        monkeypatch.setenv(f"ATTN_BF16_D{d}_WAVES", waves)
     w = W.Workload("random", B, H, N_q, N_kv, d, dt, causal, chunks,
                    seed=7000 + CASES.index(case), q_std=q_std)
     st = [W.tensor_storage(w, t) for t in (W.Q_T, W.K_T, W.V_T)]
