@@ -786,7 +786,8 @@ hipError_t launch_p3(const FwdArgs& a, hipStream_t st) {
 // (fewer than 3072 keys), where 128-row workgroups fill the chip and balance the diagonal better.  Measured
 // at d = 128 against four waves with the length-major order of causal launches: +4 to +14 % on causal rows
 // of 3072 to 8192 keys, +2 to +6 % without a mask from 1 to 8 tiles per CU, -4 to -6 % on causal rows of 1024
-// and 2048 keys at 4 tiles per CU; at d = 64, +1.7 % on 16384 keys without a mask.  ATTN_BF16_D128_WAVES and
+// and 2048 keys at 4 tiles per CU.  At d = 64: eight waves +1 to +4 % on causal rows of 4096 and 8192 keys and
+// without a mask, four waves +4 to +7.5 % on causal rows of 512 to 2048 keys.  ATTN_BF16_D128_WAVES and
 // ATTN_BF16_D64_WAVES (4 or 8) force one of them (used by the tests to run every shape through both).
 static int bf16_waves(const FwdArgs& a) {
     if (const char* e = getenv(a.d == 128 ? "ATTN_BF16_D128_WAVES" : "ATTN_BF16_D64_WAVES")) {

@@ -594,6 +594,19 @@ def test_peaky_16k():
     check_every_row(w, o_ref, l_ref, o, lse, what="peaky_16k every row")
 
 
+def test_causal_d64_prefill_every_row():
+    """The d = 64 kernel on long causal rows (B4 H16, 4096 queries and keys, logits with std 4, so that single keys
+    dominate rows and the denominator of the rounded weights matters): every row of every head against the
+    oracle's blockwise form, and seeded rows against its plain form."""
+    w = W.Workload("causal_d64_4k", 4, 16, 4096, 4096, 64, "bf16", True, 1, seed=4100, q_std=4.0)
+    st, (q, k, v) = make(w)
+    o, lse = A.fwd(q, k, v, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    check_sampled(w, st, o, lse, what="causal_d64_4k sampled")
+    o_ref, l_ref = oracle_every_row(w, st)
+    check_every_row(w, o_ref, l_ref, o, lse, what="causal_d64_4k every row")
+
+
 def test_ring_share_128k_chunked():
     """The chunked step the bench times (8 chunks folded in the forward epilogues) and the single pass, each
     compared on every row of every head against the oracle's single-pass blockwise result."""
