@@ -176,13 +176,19 @@ struct P3 {
     // d = 64 divides O by the fp32 sum of the weights' bf16 roundings (a second denominator, one dot2 per
     // weight pair); d = 128 by the fp32 sum of the weights
     static constexpr bool LT = D == 64;
-    static constexpr int SEGS = TILE / 1024, SEGS_PER_WAVE = SEGS / NW;
+    // Waves that load the tiles: in eight-wave workgroups only waves 0 .. 3 (one per SIMD), each issuing twice
+    // the loads, so that the other wave of each SIMD goes from the barrier straight into its next step; the two
+    // waves of a SIMD then start their steps a little apart (+0.8 % ring share, +1.8 % causal prefill 4k, +0.1 %
+    // peaky 16k against all eight loading, same box).  The staggered alternative, the second wave of every
+    // SIMD taking its barrier half a step later, measured -3 to -5 %.
+    static constexpr int LOADERS = NW == 8 ? NW / 2 : NW;
+    static constexpr int SEGS = TILE / 1024, SEGS_PER_WAVE = SEGS / LOADERS;   // load segments per loading wave
     static constexpr int RPS = 1024 / ROW, LPR = ROW / 16;
     // K and V buffers: K_j is loaded NK-2 steps and V_j NV-1 steps before its first use
     static constexpr int NK = NW == 8 ? 4 : 3, NV = NW == 8 ? 4 : 2;
     static constexpr int EXTRA = NK + NV >= NW + 1 ? 0 : NW + 1 - NK - NV;   // staging-only buffers
     static constexpr int LDS = (NK + NV + EXTRA) * TILE;
-    static constexpr int WSTRIDE = NW * RPS * ROW;   // bytes between the load segments of one wave
+    static constexpr int WSTRIDE = LOADERS * RPS * ROW;   // bytes between the load segments of one wave
     // retire(t) needs K_{t+2} (issued by retire(t+2-NK)) and V_{t+VAHEAD} (by retire(t+VAHEAD+1-NV)) to have
     // landed; loads are issued K then V per retire, and AFTER load instructions issued after the later of the
     // two may still be in flight.  VAHEAD = 1: eight-wave steps read the first V operands of the next step
@@ -261,24 +267,24 @@ __global__ __launch_bounds__((P3<NW, D_>::THREADS), 2) void fwd_p3_kernel(FwdArg
         v_voff = r0 * T::ROW + 16 * (p ^ v_swz<D>(r0));
     }
     auto load_k = [&](int j) __attribute__((always_inline)) {   // K_j into K buffer j % NK
-        if (j >= ntiles) return;
+        if (j >= ntiles || wave >= T::LOADERS) return;
         lds_char* buf = lds + (j % T::NK) * T::TILE;
         const long long base = (long long)j * T::TILE;
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)kh + base), (short)0, (int)(kv_bytes - base), BUF_RSRC_WORD3);
 #pragma unroll
         for (int k = 0; k < T::SEGS_PER_WAVE; ++k)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (wave + T::NW * k) * 1024), 16, k_voff, WS * k, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (wave + T::LOADERS * k) * 1024), 16, k_voff, WS * k, 0, 0);
     };
     auto load_v = [&](int j) __attribute__((always_inline)) {   // V_j into V buffer j % NV
-        if (j >= ntiles) return;
+        if (j >= ntiles || wave >= T::LOADERS) return;
         lds_char* buf = lds + (T::NK + (j % T::NV)) * T::TILE;
         const long long base = (long long)j * T::TILE;
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)vh + base), (short)0, (int)(kv_bytes - base), BUF_RSRC_WORD3);
 #pragma unroll
         for (int k = 0; k < T::SEGS_PER_WAVE; ++k)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (wave + T::NW * k) * 1024), 16, v_voff, WS * k, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (wave + T::LOADERS * k) * 1024), 16, v_voff, WS * k, 0, 0);
     };
     // Buffer bases pass through an empty statement as scalars, so that the compiler cannot split a constant
     // out of them into every read's address (it would be negative, which the offset field cannot hold).
