@@ -192,7 +192,7 @@ struct P3 {
     // retire(t) needs K_{t+2} (issued by retire(t+2-NK)) and V_{t+VAHEAD} (by retire(t+VAHEAD+1-NV)) to have
     // landed; loads are issued K then V per retire, and AFTER load instructions issued after the later of the
     // two may still be in flight.  VAHEAD = 1: eight-wave steps read the first V operands of the next step
-    // before the barrier that ends them, so V_{t+1} must have landed (in every wave) by retire(t) already
+    // before the barrier that ends them, so V_{t+1} must have landed (every loading wave's share) by retire(t)
     static constexpr int VAHEAD = NW == 8 ? 1 : 0;
     static constexpr int DK = NK - 2, DV = NV - 1 - VAHEAD;
     static_assert(DV >= 1, "V is loaded at least one step before it is needed");
@@ -553,9 +553,9 @@ __global__ __launch_bounds__((P3<NW, D_>::THREADS), 2) void fwd_p3_kernel(FwdArg
             }
         }
     };
-    // End of step t: every wave's loads of K_{t+2} and V_{t+VAHEAD} have landed and every wave is done with K_t
-    // and V_{t-1}; K_{t+NK} and V_{t+NV-1} then go into their buffers.  All waves run exactly ntiles such
-    // barriers.
+    // End of step t: the loads of K_{t+2} and V_{t+VAHEAD} have landed (each loading wave waits for its own
+    // before the barrier) and every wave is done with K_t and V_{t-1}; K_{t+NK} and V_{t+NV-1} then go into
+    // their buffers.  All waves run exactly ntiles such barriers.
     auto retire = [&](int t) __attribute__((always_inline)) {
         // K_{t+2} and V_{t+VAHEAD} were issued steps ago; the loads of the later retires may still fly (when
         // all of them exist; near the end, and after step 0, whose lead loads the prologue issued in another
