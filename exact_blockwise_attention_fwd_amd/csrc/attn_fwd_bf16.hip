@@ -196,8 +196,10 @@ struct P3 {
     static constexpr int VAHEAD = NW == 8 ? 1 : 0;
     static constexpr int DK = NK - 2, DV = NV - 1 - VAHEAD;
     static_assert(DV >= 1, "V is loaded at least one step before it is needed");
+    // (AFTER goes into the low four vmcnt bits of the s_waitcnt immediate, so it must stay below 16)
     static constexpr int AFTER = (DK < DV ? 1 + 2 * (DK - 1) : 2 * (DV - 1)) * SEGS_PER_WAVE;
     static constexpr int LEAD = NK > NV - 1 ? NK : NV - 1;   // all loads up to retire(t-1) exist iff t-1+LEAD < ntiles
+    static_assert(AFTER < 16, "loads allowed in flight fit the s_waitcnt vmcnt field");
     static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
     static_assert(D == 64 || D == 128, "head dimension 64 or 128");
     static_assert(EXP_PER_PV * NPV == 16 * NKB && PAIRS_PER_S * NS == 8 * NKB, "scores spread evenly");
