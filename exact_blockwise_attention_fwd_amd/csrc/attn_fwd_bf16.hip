@@ -439,8 +439,9 @@ __global__ __launch_bounds__((P3<NW, D_>::THREADS), 2) void fwd_p3_kernel(FwdArg
         // ---- part 1: P.V(t-1) (two transpose reads per MFMA, two MFMAs ahead) with the exps of tile t.
         // The wave runs part 1, which carries most of the step's VALU work, at raised priority and part 2 at the
         // base one: where the two waves of a SIMD are in different parts, the exponentials issue first and the
-        // other wave's S MFMAs keep the matrix pipe busy meanwhile (+0.8 to +1.0 % against no priorities;
-        // raising part 2 instead, or one wave of each pair throughout, measured -0.1 and +-0 %).
+        // other wave's S MFMAs keep the matrix pipe busy meanwhile.  Against no priorities: +2.0 % at d = 64
+        // (peaky 16k); at d = 128 +0.8 to +1.0 % while all eight waves loaded tiles, +-0 since only waves 0 .. 3
+        // do.  Raising part 2 instead measured -1.5 % at d = 64 and -0.6 % at d = 128.
         __builtin_amdgcn_s_setprio(1);
         {
             i16x4 vl[T::NPV], vhh[T::NPV];
