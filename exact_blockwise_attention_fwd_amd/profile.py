@@ -18,6 +18,8 @@ produced them and the build fingerprint of the forward kernel (its source and co
   counters  GRBM_GUI_ACTIVE and SQ counters per forward launch: MFMA busy fraction, effective engine clock,
             MFMA FLOP per algorithmic FLOP, VALU co-issue beside MFMA, VALU and LDS instructions per MFMA, LDS
             bank conflicts, and the scratch (spill) bytes per lane the dispatch ran with.
+  ffn       the blockwise feed-forward leg of the ring-share bench (its two GEMM kernels): a kernel trace, one
+            pass of the SQ counters above, and FETCH_SIZE / WRITE_SIZE against the GEMMs' algorithmic bytes.
 
 The ``key: value`` lines at the end of the traffic and counter summaries are read back by bench.py, which
 reports them only when the fingerprint matches the library it runs.
@@ -400,9 +402,95 @@ def streamed(raw: str) -> str:
     return "\n".join(lines)
 
 
+# --------------------------------------------------------------------------------------------- feed-forward
+def ffn(raw: str) -> str:
+    """The two GEMM kernels of the bench's feed-forward leg (ring-share model shape): durations, counters and
+    HBM bytes against the algorithmic ones (each operand read once, the output written once)."""
+    sys.path.insert(0, ROOT)
+    import workloads as W
+    from exact_blockwise_attention_fwd_amd.build import fingerprint as fp
+
+    fw = W.FFN_WORKLOADS["ffn_ring_share"]
+    fpr = fp("ffn_bf16.hip")
+    args = ["--workload", "ring_share_128k", "--steps", "1", "--warmup", "0", "--no-cpu-baseline", "--no-streamed",
+            "--no-graph", "--no-ulysses"]
+    copy_args = ["--calibrate-copy", "--steps", "2", "--warmup", "1"]
+    tr, tr_cmd = run_profiled("ffn_trace", ["--kernel-trace", "--stats"], args, raw, 300)
+    sq, sq_cmd = run_profiled("ffn_counters", ["--pmc", *SQ_COUNTERS], args, raw, 150)
+    runs = {t: run_profiled(f"ffn_{t}", ["--pmc", c], a, raw, 120)
+            for t, c, a in (("fetch", "FETCH_SIZE", args), ("write", "WRITE_SIZE", args),
+                            ("fetch_copy", "FETCH_SIZE", copy_args), ("write_copy", "WRITE_SIZE", copy_args))}
+
+    def per_kernel(tag, ctr, pred):
+        return [float(col(r, "Counter_Value")) for r in counter_rows(runs[tag][0], ctr) if pred(col(r, "Kernel_Name"))]
+
+    is_copy = lambda k: "copy" in k.lower()
+    fcopy, wcopy = per_kernel("fetch_copy", "FETCH_SIZE", is_copy), per_kernel("write_copy", "WRITE_SIZE", is_copy)
+    f_fac = COPY_BYTES / (sum(fcopy) / len(fcopy) * 1024) if fcopy else float("nan")
+    w_fac = COPY_BYTES / (sum(wcopy) / len(wcopy) * 1024) if wcopy else float("nan")
+    flop = 2.0 * fw.block * fw.d_ff * fw.d_model   # per GEMM launch, either product
+    kernels = [("gemm_nt_kernel<2>", "x W1^T + b1, GELU", fw.block * fw.d_model * 2 + fw.d_ff * fw.d_model * 2,
+                fw.block * fw.d_ff * 2),
+               ("gemm_nt_kernel<0>", "h W2^T + b2", fw.block * fw.d_ff * 2 + fw.d_model * fw.d_ff * 2,
+                fw.block * fw.d_model * 2)]
+    disp = {}
+    for r in read_csv(sq, "counter_collection.csv"):
+        k = col(r, "Kernel_Name")
+        if "gemm_nt_kernel" not in k:
+            continue
+        d = disp.setdefault(int(col(r, "Correlation_Id", "Dispatch_Id")), {"kernel": k})
+        d[col(r, "Counter_Name")] = float(col(r, "Counter_Value"))
+        for key, names in (("start", ("Start_Timestamp",)), ("end", ("End_Timestamp",))):
+            try:
+                d[key] = float(col(r, *names))
+            except (KeyError, ValueError):
+                pass
+    stats = {short(col(r, "Name", "Kernel_Name")): r for r in read_csv(tr, "kernel_stats.csv")}
+    lines = ["# Blockwise feed-forward (attn_ffn_blockwise), ring-share model shape: kernel trace, counters, traffic", "",
+             f"GEMM kernel build fingerprint (source and compile flags): `{fpr}`", "",
+             f"Shape: M = {fw.M} rows, d_model = {fw.d_model}, d_ff = {fw.d_ff}, {fw.act}, blocks of {fw.block} rows:",
+             f"per block one GEMM of {fw.block} x {fw.d_ff} x {fw.d_model} with the bias + activation epilogue and one of",
+             f"{fw.block} x {fw.d_model} x {fw.d_ff} with the bias epilogue; {flop:.4e} FLOP each.  The bench's ffn leg",
+             "runs 2 warmup calls and 10 timed ones.  Commands (the copy runs calibrate FETCH_SIZE and WRITE_SIZE on a",
+             "plain 1 GiB device-to-device copy):", "", f"    {tr_cmd}", f"    {sq_cmd}"]
+    lines += [f"    {runs[t][1]}" for t in ("fetch", "write", "fetch_copy", "write_copy")]
+    b = bench_json(tr)
+    if b and b.get("ffn"):
+        f = b["ffn"]
+        lines += ["", f"bench line under the profiler: {f.get('ms')} ms per call = {f.get('tflops')} TFLOP/s "
+                      f"({f.get('gemm_launches')} GEMM launches per call averaging {f.get('gemm_ms_avg')} ms)"]
+    lines += ["", "| kernel | calls | avg us | min us | TFLOP/s (avg) | sclk GHz | MFMA busy | LDS / MFMA | "
+                  "HBM read / algorithmic | HBM written / algorithmic |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for name, what, alg_r, alg_w in kernels:
+        st = stats.get(name)
+        if st is None:
+            continue
+        avg = float(col(st, "AverageNs")) / 1e3
+        mn = float(col(st, "MinNs")) / 1e3 if "MinNs" in st else float("nan")
+        ds = [d for d in disp.values() if short(d["kernel"]) == name]
+        busy = sclk = lm = float("nan")
+        try:
+            us = [(d["end"] - d["start"]) * 1e-3 for d in ds]
+            gui = [d["GRBM_GUI_ACTIVE"] / 8 for d in ds]
+            sclk = sum(g / (u * 1e3) for g, u in zip(gui, us)) / len(ds)
+            busy = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * 1024) for d, g in zip(ds, gui)) / len(ds)
+            lm = sum(d["SQ_INSTS_LDS"] / max(d["SQ_INSTS_MFMA"], 1) for d in ds) / len(ds)
+        except (KeyError, ZeroDivisionError):
+            pass
+        pred = lambda k, name=name: short(k) == name
+        fr, wr = per_kernel("fetch", "FETCH_SIZE", pred), per_kernel("write", "WRITE_SIZE", pred)
+        rd = sum(fr) / len(fr) * 1024 * f_fac if fr else float("nan")
+        wt = sum(wr) / len(wr) * 1024 * w_fac if wr else float("nan")
+        lines.append(f"| `{name}` ({what}) | {col(st, 'Calls')} | {avg:.1f} | {mn:.1f} | {flop / (avg * 1e-6) / 1e12:.0f} | "
+                     f"{sclk:.2f} | {busy:.3f} | {lm:.2f} | {rd:.3e} / {alg_r:.3e} | {wt:.3e} / {alg_w:.3e} |")
+    lines += ["", f"Counter pass: {len(disp)} GEMM dispatches; copy calibration: FETCH_SIZE factor {f_fac:.4f}, "
+                  f"WRITE_SIZE factor {w_fac:.4f}.  Definitions as in attn_fwd_bf16_counters.txt.", ""]
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--what", default="trace,traffic,counters,streamed")
+    ap.add_argument("--what", default="trace,traffic,counters,streamed,ffn")
     ap.add_argument("--workloads", default="ring_share_128k,ulysses_share_256k,causal_prefill_4k,peaky_16k,tiny_fp32")
     ap.add_argument("--steps", type=int, default=None, help="timed steps of every trace run (default: per workload)")
     ap.add_argument("--warmup", type=int, default=None, help="warmup steps of every trace run (default: per workload)")
@@ -424,6 +512,9 @@ def main():
     if "streamed" in what:
         open(os.path.join(a.out, "attn_fwd_streamed_ring_share_128k.md"), "w").write(streamed(a.raw))
         log("wrote attn_fwd_streamed_ring_share_128k.md")
+    if "ffn" in what:
+        open(os.path.join(a.out, "ffn_bf16_ring_share.md"), "w").write(ffn(a.raw))
+        log("wrote ffn_bf16_ring_share.md")
     if "counters" in what:
         for n in names:
             if workload(n).dtype != "bf16":
