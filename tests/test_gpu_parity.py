@@ -275,6 +275,40 @@ def test_peaky_sorted_keys_rescale_every_tile(d):
     assert_parity(errors(out_to_f64(o), out_to_f64(lse), o_ref, l_ref), "bf16", "sorted keys")
 
 
+@pytest.mark.parametrize("waves", ["4", "8"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_stale_reference_envelope(d, waves, monkeypatch):
+    """The exponent reference stays at the row max of the first key tile here: every later tile holds one key about
+    63 exp2-units above it, just under the 2^64 weight-sum bound that would move it, and that key's V entries are
+    near 2^58.  The fp32 accumulators then reach ~2^125.5, near the edge of the envelope the bf16 kernel states for
+    its stale reference (at most 2^64 per tile x tiles x max|V|, below 2^128).  The result still matches the oracle
+    (which keeps the running max), compared in units of 2^58."""
+    monkeypatch.setenv(f"ATTN_BF16_D{d}_WAVES", waves)
+    B, H, nq, nkv = 1, 2, 64, 1024
+    scale = 1.0 / math.sqrt(d)
+    c = scale * math.log2(math.e)
+    rng = np.random.default_rng(2300 + d)
+    q = np.zeros((B, H, nq, d), np.float32)
+    q[..., 0] = 1.0
+    q[..., 1] = rng.choice([-0.5, 0.5], (B, H, nq))
+    k = np.zeros((B, H, nkv, d), np.float32)
+    k[..., 1] = rng.choice([-1.0, 1.0], (B, H, nkv))
+    big = 64 * np.arange(1, nkv // 64) + rng.integers(0, 64, nkv // 64 - 1)   # one key in every tile after the first
+    k[:, :, big, 0] = np.float32(round(63.0 / c))
+    v = rng.standard_normal((B, H, nkv, d)).astype(np.float32)
+    v[:, :, big, :] = np.float32(2.0 ** 58) * rng.choice([0.75, 1.0, 1.25, 1.5], (B, H, len(big), d)).astype(np.float32)
+    st = [W.f32_to_bf16_bits(x) for x in (q, k, v)]
+    qq, kk, vv = (storage_to_f64(x) for x in st)
+    top = (kk[0, 0, big, 0] - 0.5) * c   # the big keys' exponents against the first tile's max (0.5)
+    assert top.max() < 64.0 and top.min() > 62.0, "the test keys sit just under the bound that moves the reference"
+    o_ref, l_ref = oracle.attention(qq, kk, vv, scale, False, nkv - nq)
+    o, lse = A.fwd(*(to_device(x) for x in st), causal=False, scale=scale)
+    torch.cuda.synchronize()
+    err = errors(out_to_f64(o) / 2.0 ** 58, out_to_f64(lse), o_ref / 2.0 ** 58, l_ref)
+    print(f"d={d} waves={waves}", err, flush=True)
+    assert_parity(err, "bf16", f"envelope d={d} waves={waves}")
+
+
 def test_key_range_and_offset_partials():
     """attn_fwd_ex over two key ranges (fp32 partials with explicit offsets) merged = the whole."""
     w = W.Workload("ranges", 1, 2, 384, 1000, 128, "bf16", True, 1, seed=2200)
