@@ -5,12 +5,13 @@
 // exactness: no fp32 matrix cores (gfx950 has no xf32 MFMA) and accurate expf/logf.  Dot products, scaled
 // logits and the running max are kept in fp64, so that the rounding of an fp32 dot product (which grows
 // with the logit magnitude) does not reach the softmax weights; weights, the denominator and the output
-// accumulate in fp32.
+// accumulate in fp32, per key tile first and then across tiles.
 //
 // The problems this path serves are small, so the kernel is built for latency:
 //  * LPR lanes share a query row (4, 8 or 16), each holding DMAX/LPR head-dim elements in float4 chunks;
-//    a workgroup of 256 lanes owns 256/LPR rows.  The launch takes the fewest lanes per row that still give
-//    two workgroups per CU, so small launches spread over the chip with short per-lane dot products.
+//    a workgroup of 256 lanes owns 256/LPR rows.  The launch takes the fewest lanes per row (at least 8 from
+//    d = 128 up) that still give two workgroups per CU, so small launches spread over the chip with short
+//    per-lane dot products.
 //  * K/V tiles of 32 keys (16 at d > 128, which keeps LDS at 64 KiB) are double-buffered in LDS, zero padded
 //    past d and past the last key.  The global loads of tile t+1 are issued into registers before tile t is
 //    computed and land in the other buffer after it, so load latency hides under the arithmetic; one
@@ -36,6 +37,7 @@ __global__ __launch_bounds__(F_THREADS) void fwd_f32_kernel(FwdArgs a, int num_q
     constexpr int NCH = DMAX / (4 * LPR);          // float4 chunks per lane
     constexpr int C4 = DMAX / 4;                   // float4 chunks per K/V row in LDS
     constexpr int LOADS = F_TKV * C4 / F_THREADS;  // float4 chunks of one tile each thread loads, per tensor
+    constexpr int SUB = F_TKV;                     // keys whose weights are summed apart before joining the row's sums
     static_assert(NCH >= 1 && LOADS >= 1 && F_TKV * C4 % F_THREADS == 0, "tile split");
     __shared__ f32x4 ks[2][F_TKV][C4];
     __shared__ f32x4 vs[2][F_TKV][C4];
@@ -114,45 +116,56 @@ __global__ __launch_bounds__(F_THREADS) void fwd_f32_kernel(FwdArgs a, int num_q
         const int b = t & 1;
         if (t + 1 < ntiles) fetch(t + 1);          // in flight while tile t is computed
 
-        double s[F_TKV];
-        double mt = -INFINITY;
-        const int kt = t * F_TKV;
 #pragma unroll
-        for (int j = 0; j < F_TKV; ++j) {
-            double part = 0.0;
+        for (int h0 = 0; h0 < F_TKV; h0 += SUB) {   // keys h0 .. h0+SUB-1 of the tile
+            double s[SUB];
+            double mt = -INFINITY;
+            const int kt = t * F_TKV + h0;
 #pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-                const f32x4 k4 = ks[b][j][LPR * i + r];
-                part = fma((double)q[i][0], (double)k4[0], part);
-                part = fma((double)q[i][1], (double)k4[1], part);
-                part = fma((double)q[i][2], (double)k4[2], part);
-                part = fma((double)q[i][3], (double)k4[3], part);
-            }
-#pragma unroll
-            for (int w = 1; w < LPR; w *= 2) part += __shfl_xor(part, w, 64);
-            s[j] = (kt + j <= lim) ? part * (double)a.scale : -INFINITY;
-            mt = fmax(mt, s[j]);
-        }
-        const double m_new = fmax(m, mt);
-        if (m_new != -INFINITY) {                  // else nothing visible yet for this row
-            const float alpha = m == -INFINITY ? 0.f : expf((float)(m - m_new));
-            l *= alpha;
-#pragma unroll
-            for (int i = 0; i < NCH; ++i) acc[i] *= alpha;
-#pragma unroll
-            for (int j = 0; j < F_TKV; ++j) {
-                const float p = expf((float)(s[j] - m_new));   // exp(-inf) = 0 for masked keys
-                l += p;
+            for (int j = 0; j < SUB; ++j) {
+                double part = 0.0;
 #pragma unroll
                 for (int i = 0; i < NCH; ++i) {
-                    const f32x4 v4 = vs[b][j][LPR * i + r];
-                    acc[i][0] = fmaf(p, v4[0], acc[i][0]);
-                    acc[i][1] = fmaf(p, v4[1], acc[i][1]);
-                    acc[i][2] = fmaf(p, v4[2], acc[i][2]);
-                    acc[i][3] = fmaf(p, v4[3], acc[i][3]);
+                    const f32x4 k4 = ks[b][h0 + j][LPR * i + r];
+                    part = fma((double)q[i][0], (double)k4[0], part);
+                    part = fma((double)q[i][1], (double)k4[1], part);
+                    part = fma((double)q[i][2], (double)k4[2], part);
+                    part = fma((double)q[i][3], (double)k4[3], part);
                 }
+#pragma unroll
+                for (int w = 1; w < LPR; w *= 2) part += __shfl_xor(part, w, 64);
+                s[j] = (kt + j <= lim) ? part * (double)a.scale : -INFINITY;
+                mt = fmax(mt, s[j]);
             }
-            m = m_new;
+            const double m_new = fmax(m, mt);
+            if (m_new != -INFINITY) {                  // else nothing visible yet for this row
+                const float alpha = m == -INFINITY ? 0.f : expf((float)(m - m_new));
+                // These keys' weights and weighted rows are summed apart (chains of SUB terms) and join the running
+                // sums once, so a row's rounding grows with its count of tiles rather than of keys.
+                float lt = 0.f;
+                f32x4 at[NCH];
+#pragma unroll
+                for (int i = 0; i < NCH; ++i) at[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < SUB; ++j) {
+                    const float p = expf((float)(s[j] - m_new));   // exp(-inf) = 0 for masked keys
+                    lt += p;
+#pragma unroll
+                    for (int i = 0; i < NCH; ++i) {
+                        const f32x4 v4 = vs[b][h0 + j][LPR * i + r];
+                        at[i][0] = fmaf(p, v4[0], at[i][0]);
+                        at[i][1] = fmaf(p, v4[1], at[i][1]);
+                        at[i][2] = fmaf(p, v4[2], at[i][2]);
+                        at[i][3] = fmaf(p, v4[3], at[i][3]);
+                    }
+                }
+                l = fmaf(l, alpha, lt);
+#pragma unroll
+                for (int i = 0; i < NCH; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(acc[i][e], alpha, at[i][e]);
+                m = m_new;
+            }
         }
         // Buffer b^1 was last read in iteration t-1, which every wave finished before the barrier that
         // ended it; the barrier below keeps iteration t+1 from reading it before every wave stored it.
@@ -204,7 +217,10 @@ hipError_t launch_t(const FwdArgs& a, int vec_loads, hipStream_t s) {
     return hipGetLastError();
 }
 
-// The fewest lanes per row (4, 8, 16; at most DMAX/4) that still give two workgroups per CU.
+// The fewest lanes per row (4, 8, 16; at most DMAX/4) that still give two workgroups per CU, and at least 8
+// from 128 elements up: four lanes per row there need more registers than two waves per SIMD hold (measured
+// against four: +124 % at d = 256 on a 4096-row launch; -25 % at d = 128, where four lanes fitted two waves
+// before each key tile got its own partial sums).
 // ATTN_F32_LANES_PER_ROW=4, 8 or 16 forces one where the head dimension allows it (used by the tests to run
 // every shape through each).
 template <int DMAX>
@@ -217,7 +233,7 @@ hipError_t launch_d(const FwdArgs& a, int vec_loads, hipStream_t s) {
     if (lpr == 0) {
         const long long want = 2LL * device_cus();
         auto groups = [&](int l) { return (long long)((a.n_q + F_THREADS / l - 1) / (F_THREADS / l)) * a.bh; };
-        lpr = groups(4) >= want ? 4 : (DMAX < 64 || groups(8) >= want) ? 8 : 16;
+        lpr = (DMAX <= 64 && groups(4) >= want) ? 4 : (DMAX < 64 || groups(8) >= want) ? 8 : 16;
     }
     if constexpr (DMAX >= 64) {
         if (lpr == 16) return launch_t<DMAX, 16>(a, vec_loads, s);
