@@ -220,6 +220,32 @@ def test_f32_lanes_per_row(case, lanes, monkeypatch):
     assert_parity(errors(out_to_f64(oc), out_to_f64(lc), o_ref, l_ref), "f32", f"{w} lanes={lanes} 3 chunks")
 
 
+# Long rows with peaky logits (std 6) in fp32: the weighted rows are summed per key tile before they join the running
+# sums, so the rounding grows with the number of tiles, not of keys (summed key by key, the second and third shapes
+# reached max-abs 2.1e-5 and 1.6e-5 against the 1e-5 bar, at every lanes-per-row choice).
+F32_PEAKY = [
+    # B, H, N_q, N_kv, d
+    (2, 1, 78, 2187, 8),
+    (1, 2, 200, 4000, 64),
+    (1, 1, 130, 3000, 128),
+]
+
+
+@pytest.mark.parametrize("lanes", ["4", "8", "16"])
+@pytest.mark.parametrize("case", F32_PEAKY, ids=lambda c: "x".join(map(str, c)))
+def test_f32_long_peaky_rows(case, lanes, monkeypatch):
+    B, H, N_q, N_kv, d = case
+    monkeypatch.setenv("ATTN_F32_LANES_PER_ROW", lanes)
+    w = W.Workload("f32peaky", B, H, N_q, N_kv, d, "f32", False, 1, seed=5100 + d, q_std=6.0)
+    st, (q, k, v) = make(w)
+    o_ref, l_ref = oracle_full(st, w)
+    o, lse = A.fwd(q, k, v, causal=False, scale=w.scale)
+    torch.cuda.synchronize()
+    err = errors(out_to_f64(o), out_to_f64(lse), o_ref, l_ref)
+    print(w.name, case, lanes, err, flush=True)
+    assert_parity(err, "f32", f"{case} lanes={lanes}")
+
+
 def test_f32_large_launch():
     """An fp32 launch large enough for four lanes per row on its own (1024 workgroups of 64 rows), with
     tiles in flight across many steps: sampled rows against the oracle."""
