@@ -23,7 +23,7 @@ from parity import assert_parity, errors, out_to_f64, storage_to_f64, to_device
 pytestmark = pytest.mark.gpu
 
 
-def _cases(n: int = 60):
+def _cases(n: int = 90):
     rng = np.random.default_rng(20261203)
     out = []
     for i in range(n):
@@ -34,7 +34,9 @@ def _cases(n: int = 60):
         N_q = int(rng.choice([int(rng.integers(1, 64)), int(rng.integers(64, 700))]))
         N_kv = int(rng.choice([int(rng.integers(1, 64)), int(rng.integers(64, 1500))]))
         causal = bool(rng.integers(0, 2))
-        q_std = float(rng.choice([1.0, 1.0, 3.0]))
+        # logits up to std 6, except bf16 at d = 128, whose output is divided by the fp32 weight sum (a single
+        # dominant key's bf16 rounding then stays in O; every d = 128 workload has logits with std 1)
+        q_std = float(rng.choice([1.0, 1.0, 3.0] if (dt == "bf16" and d == 128) else [1.0, 3.0, 6.0]))
         chunks = int(rng.choice([1, 1, 2, 5]))
         waves = ("4" if i % 2 else "8") if dt == "bf16" else None
         out.append((B, H, N_q, N_kv, d, dt, causal, q_std, chunks, waves))
