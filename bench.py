@@ -153,6 +153,27 @@ def time_merge(w, reps: int):
     return ms / max(n, 1)
 
 
+def time_copy(nbytes: int, reps: int) -> float:
+    """GB/s of a plain device-to-device copy of nbytes (read + written bytes per second): the practical HBM
+    ceiling the merge's GB/s is read against, measured in the same job."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def time_streamed(w, q, k, v, steps: int, compute_ms: float):
     """The same chunked step with K and V in page-locked host memory (attn_fwd_streamed): chunk p+1 is copied
     to the device on a second stream while chunk p computes.  Times the step with events on the compute
@@ -578,7 +599,10 @@ def main():
     merge_ms = time_merge(w, 10)
     mb = merge_bytes(w)
     merge_gbs = mb / (merge_ms * 1e-3) / 1e9 if merge_ms > 0 else None
-    log(f"attn_merge alone: {merge_ms:.4f} ms, {merge_gbs:.1f} GB/s")
+    copy_gbs = time_copy(1 << 30, 10)
+    log(f"attn_merge alone: {merge_ms:.4f} ms, {merge_gbs:.1f} GB/s; 1 GiB device copy {copy_gbs:.1f} GB/s")
+    # one exponential per visible (query, key) pair; not counted in the FLOPs
+    pairs = w.B * w.H * w.visible_pairs()
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -590,11 +614,13 @@ def main():
         "step_ms": {"median": round(per_step[len(per_step) // 2], 4), "min": round(per_step[0], 4),
                     "max": round(per_step[-1], 4)},
         "fwd_kernel": {"launches_per_step": n_fwd / args.steps, "ms_per_step": fwd_ms / args.steps,
-                       "tflops": None if fwd_tflops is None else round(fwd_tflops, 2)},
+                       "tflops": None if fwd_tflops is None else round(fwd_tflops, 2),
+                       "exp_per_s": None if fwd_ms <= 0 else float(f"{pairs * args.steps / (fwd_ms * 1e-3):.4e}")},
         "merge": None if merge_gbs is None else {
             "what": "attn_merge alone, fp32 partials in place, rows = B*H*N_q", "rows": w.B * w.H * w.N_q,
             "ms": round(merge_ms, 4), "bytes": mb, "gbs": round(merge_gbs, 1),
-            "pct_hbm_peak": round(100 * merge_gbs / HBM_PEAK_GBS, 2)},
+            "pct_hbm_peak": round(100 * merge_gbs / HBM_PEAK_GBS, 2),
+            "device_copy_gbs": round(copy_gbs, 1), "frac_of_device_copy": round(merge_gbs / copy_gbs, 4)},
         "roofline": {"bound": "mfma", "achieved": None if fwd_tflops is None else round(fwd_tflops, 2),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": None if fwd_tflops is None else round(fwd_tflops / BF16_PEAK_TFLOPS, 4),

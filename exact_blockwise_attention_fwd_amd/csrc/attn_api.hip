@@ -434,15 +434,19 @@ int run_chunked(const FwdCheck& c, const void* Q, const void* K, const void* V, 
         if (overlap(workspace, need, others[i], other_n[i]))
             return fail(ATTN_ERR_BAD_ALIAS, "workspace overlaps Q, K, V, O or LSE");
 
-    // chunk p covers keys [floor(p*N_kv/P), floor((p+1)*N_kv/P)); empty or wholly-future chunks are skipped
-    std::vector<int> live;
-    for (int p = 0; p < P; ++p) {
+    // chunk p covers keys [floor(p*N_kv/P), floor((p+1)*N_kv/P)); empty or wholly-future chunks are skipped.
+    // The live chunks are found by a scan, not stored, so that the call allocates no host memory either.
+    auto is_live = [&](int p) {
         const long long lo = (long long)p * N_kv / P, hi = (long long)(p + 1) * N_kv / P;
-        if (hi == lo) continue;
-        if (causal && (long long)N_q - 1 + offset - lo < 0) continue;
-        live.push_back(p);
-    }
-    if (live.empty()) live.push_back(0);   // unreachable with offset N_kv - N_q; kept for safety
+        return hi != lo && !(causal && (long long)N_q - 1 + offset - lo < 0);
+    };
+    int first = -1, last = -1;
+    for (int p = 0; p < P; ++p)
+        if (is_live(p)) {
+            if (first < 0) first = p;
+            last = p;
+        }
+    if (first < 0) first = last = 0;   // unreachable with offset N_kv - N_q; kept for safety
     const size_t rows = (size_t)B * H * N_q;
     char* ws = static_cast<char*>(workspace);
     float* o_acc = reinterpret_cast<float*>(ws);
@@ -457,12 +461,12 @@ int run_chunked(const FwdCheck& c, const void* Q, const void* K, const void* V, 
         return launch_fwd(Q, kp, vp, o, lse, B, H, N_q, (int)(hi - lo), d, causal, scale, offset - lo, c.kv_stride,
                           dtype, out_t, s, prev_o, prev_lse);
     };
-    if (live.size() == 1) return chunk(live[0], O, LSE, dtype, nullptr, nullptr);
-    if ((st = chunk(live[0], o_acc, lse_acc, ATTN_F32, nullptr, nullptr))) return st;
-    for (size_t i = 1; i < live.size(); ++i) {
-        const bool last = i + 1 == live.size();
-        st = last ? chunk(live[i], O, LSE, dtype, o_acc, lse_acc)
-                  : chunk(live[i], o_acc, lse_acc, ATTN_F32, o_acc, lse_acc);
+    if (first == last) return chunk(first, O, LSE, dtype, nullptr, nullptr);
+    if ((st = chunk(first, o_acc, lse_acc, ATTN_F32, nullptr, nullptr))) return st;
+    for (int p = first + 1; p <= last; ++p) {
+        if (!is_live(p)) continue;
+        st = p == last ? chunk(p, O, LSE, dtype, o_acc, lse_acc)
+                       : chunk(p, o_acc, lse_acc, ATTN_F32, o_acc, lse_acc);
         if (st) return st;
     }
     return ATTN_OK;
