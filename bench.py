@@ -74,7 +74,122 @@ def time_graph(step, steps: int) -> float:
     return e0.elapsed_time(e1) / steps
 
 
-def time_workload(w, steps: int, warmup: int) -> dict:
+NOMINAL_SCLK_MHZ = 2400.0       # the engine clock the dense bf16 peak is quoted at
+
+
+class ClockPowerSampler:
+    """Engine clock and socket power of the measured GPU, read through amdsmi (read-only queries) every `period`
+    seconds on a host thread while a timed region runs.  Under the attention step the board sits near its
+    power cap and the clock falls below the nominal 2.4 GHz by an amount that differs from board to board;
+    these samples show what the timed region ran at.  Anything amdsmi cannot give is reported as an error
+    string, never raised."""
+
+    def __init__(self, period: float = 0.02):
+        self.period = period
+        self.samples = []
+        self.error = None
+        self.limit_w = None
+        self._h = None
+        self._thread = None
+        self._stop = None
+
+    def _handle(self):
+        import amdsmi
+        import torch
+
+        amdsmi.amdsmi_init()
+        hs = amdsmi.amdsmi_get_processor_handles()
+        if len(hs) == 1:
+            return hs[0]
+        props = torch.cuda.get_device_properties(torch.cuda.current_device())
+        bus = getattr(props, "pci_bus_id", None)
+        for h in hs:
+            bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+            if bus is not None and int(bdf.split(":")[1], 16) == bus:
+                return h
+        raise RuntimeError(f"no amdsmi handle matches the device's PCI bus ({len(hs)} handles)")
+
+    def __enter__(self):
+        import threading
+
+        try:
+            import amdsmi
+
+            self._h = self._handle()
+            lim = amdsmi.amdsmi_get_power_info(self._h).get("power_limit")
+            self.limit_w = lim / 1e6 if isinstance(lim, (int, float)) and lim > 1e5 else lim
+        except Exception as e:   # no amdsmi, no permission, no device: report, do not fail the bench
+            self.error = f"{type(e).__name__}: {e}"
+            return self
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                try:
+                    m = amdsmi.amdsmi_get_gpu_metrics_info(self._h)
+                    clks = [c for c in m.get("current_gfxclks", []) if isinstance(c, (int, float)) and c > 0]
+                    pw = m.get("current_socket_power")
+                    if clks and isinstance(pw, (int, float)):
+                        self.samples.append((time.time(), sum(clks) / len(clks), min(clks), max(clks), float(pw)))
+                except Exception as e:
+                    self.error = f"{type(e).__name__}: {e}"
+                    return
+                self._stop.wait(self.period)
+
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def summary(self, what: str, achieved_tflops=None, skip_s: float = 0.0) -> dict:
+        out = {"source": f"amdsmi gpu metrics sampled every {int(self.period * 1000)} ms over {what}, the first "
+                         f"{skip_s:g} s dropped (the board's figures lag the load by a few hundred ms)"}
+        t0 = self.samples[0][0] if self.samples else 0.0
+        sm = [x for x in self.samples if x[0] - t0 >= skip_s]
+        out["samples"] = len(sm)
+        if not sm:
+            out["error"] = self.error or "no samples"
+            return out
+        clk = sum(x[1] for x in sm) / len(sm)
+        out.update({"gfxclk_mhz_mean": round(clk, 1), "gfxclk_mhz_xcd_min": min(x[2] for x in sm),
+                    "gfxclk_mhz_xcd_max": max(x[3] for x in sm),
+                    "socket_power_w_mean": round(sum(x[4] for x in sm) / len(sm), 1),
+                    "socket_power_w_max": max(x[4] for x in sm), "power_limit_w": self.limit_w})
+        if achieved_tflops:
+            peak = BF16_PEAK_TFLOPS * clk / NOMINAL_SCLK_MHZ
+            out.update({"bf16_peak_at_sampled_clock_tflops": round(peak, 1),
+                        "frac_at_sampled_clock": round(achieved_tflops / peak, 4)})
+        return out
+
+
+CLOCK_SECONDS = 3.0   # length of the sampled run after a timed region
+CLOCK_SKIP_S = 0.8    # its first part, dropped
+
+
+def sample_clock_power(step, achieved_tflops, seconds: float = CLOCK_SECONDS) -> dict:
+    """Runs `step` back to back for about `seconds` after the timed region (the queue kept a few steps deep)
+    and samples the engine clock and socket power meanwhile."""
+    import torch
+
+    n = 0
+    with ClockPowerSampler() as power:
+        t_end = time.time() + seconds
+        while time.time() < t_end:
+            step()
+            n += 1
+            if n % 2 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+    return power.summary(f"{n} further steps of the same workload after the timed ones", achieved_tflops,
+                         CLOCK_SKIP_S)
+
+
+def time_workload(w, steps: int, warmup: int, clock_seconds: float = CLOCK_SECONDS) -> dict:
     """A second workload's step (single pass or chunked, as configured) on seeded inputs resident in HBM: ms
     per step with events on the current stream, and the forward launches' TFLOP/s from the library's events
     against the dense bf16 peak."""
@@ -115,6 +230,7 @@ def time_workload(w, steps: int, warmup: int) -> dict:
     ms = e0.elapsed_time(e1) / steps
     tf = w.flops() / (ms * 1e-3) / 1e12
     ktf = w.flops() * steps / (fwd_ms * 1e-3) / 1e12
+    clock_power = sample_clock_power(step, ktf, clock_seconds) if clock_seconds > 0 else None
     del q, k, v, o, lse, ws
     torch.cuda.empty_cache()
     return {"config": {"workload": w.name, "B": w.B, "H": w.H, "N_q": w.N_q, "N_kv": w.N_kv, "d": w.d,
@@ -122,7 +238,8 @@ def time_workload(w, steps: int, warmup: int) -> dict:
             "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4), "tflops": round(tf, 2),
             "pct_bf16_peak": round(100 * tf / BF16_PEAK_TFLOPS, 2),
             "fwd_kernel": {"launches_per_step": n_fwd / steps, "tflops": round(ktf, 2),
-                           "frac": round(ktf / BF16_PEAK_TFLOPS, 4)}}
+                           "frac": round(ktf / BF16_PEAK_TFLOPS, 4)},
+            "clock_power": clock_power}
 
 
 def time_merge(w, reps: int):
@@ -504,6 +621,8 @@ def main():
     ap.add_argument("--no-ffn", action="store_true",
                     help="skip the blockwise feed-forward leg (run with the ring-share workload only)")
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
+    ap.add_argument("--clock-seconds", type=float, default=CLOCK_SECONDS,
+                    help="length of the run after each timed region over which clock and power are sampled (0: none)")
     ap.add_argument("--no-ulysses", action="store_true",
                     help="skip the Ulysses head-share object (run with the ring-share workload only)")
     ap.add_argument("--ffn-vendor-context", action="store_true",
@@ -596,6 +715,10 @@ def main():
     value = flops / (ms * 1e-3) / 1e12
     n_fwd, fwd_ms = kt["fwd"]
     fwd_tflops = flops * args.steps / (fwd_ms * 1e-3) / 1e12 if fwd_ms > 0 else None
+    clock_power = None
+    if args.clock_seconds > 0:
+        clock_power = sample_clock_power(step, fwd_tflops if w.dtype == "bf16" else None, args.clock_seconds)
+        log(f"clock and power: {clock_power}")
     merge_ms = time_merge(w, 10)
     mb = merge_bytes(w)
     merge_gbs = mb / (merge_ms * 1e-3) / 1e9 if merge_ms > 0 else None
@@ -625,6 +748,7 @@ def main():
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": None if fwd_tflops is None else round(fwd_tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": recorded_traffic(w)},
+        "clock_power": clock_power,
         "counters": recorded_counters(w),
         "counters_source": recorded_source(COUNTERS_FILE, w),
         "traffic_source": recorded_source(TRAFFIC_FILE, w),
@@ -655,7 +779,7 @@ def main():
         log("timing the Ulysses head share (the other causal long-sequence workload)")
         del q, k, v, o, lse, ws
         torch.cuda.empty_cache()
-        out["ulysses"] = time_workload(W.WORKLOADS["ulysses_share_256k"], 5, 1)
+        out["ulysses"] = time_workload(W.WORKLOADS["ulysses_share_256k"], 5, 1, args.clock_seconds)
         log(f"ulysses: {out['ulysses']}")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")

@@ -77,6 +77,8 @@ def run_profiled(tag: str, prof_args: list[str], bench_args: list[str], raw: str
     out = os.path.join(raw, tag)
     shutil.rmtree(out, ignore_errors=True)
     os.makedirs(out, exist_ok=True)
+    if "--calibrate-copy" not in bench_args:
+        bench_args = [*bench_args, "--clock-seconds", "0"]   # no clock/power run after the profiled steps
     cmd = ["timeout", "-s", "KILL", str(limit), rocprof(), *prof_args, "--output-format", "csv", "-d", out, "-o", "run",
            "--", sys.executable, BENCH, *bench_args]
     shown = " ".join(["timeout", "-s", "KILL", str(limit), "rocprofv3", *prof_args, "--output-format", "csv", "-d",
