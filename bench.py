@@ -609,6 +609,52 @@ def recorded_counters(w):
         return None
 
 
+def live_counters(w, limit_s: int = 420):
+    """Traffic and matrix-core counters of this workload's forward launches measured in this run: the committed
+    rocprofv3 harness (python -m exact_blockwise_attention_fwd_amd.profile) runs as a child process once this
+    process has finished its own GPU work, each profiled bench step a grandchild under its own time limit.
+    Returns (traffic bytes per launch or None, counters dict or None, source dict); the source carries the
+    error text when the child failed."""
+    import shutil
+    import subprocess
+    import tempfile
+
+    from exact_blockwise_attention_fwd_amd.build import fingerprint
+
+    what = ["counters"] if w.dtype == "bf16" else []
+    if w.name == "ring_share_128k":
+        what.insert(0, "traffic")
+    if not what:
+        return None, None, {"source": "this run", "error": "no counter passes for this workload"}
+    tmp = tempfile.mkdtemp(prefix="attn_live_prof_", dir="/tmp")
+    cmd = [sys.executable, "-m", "exact_blockwise_attention_fwd_amd.profile", "--what", ",".join(what),
+           "--workloads", w.name, "--out", os.path.join(tmp, "out"), "--raw", os.path.join(tmp, "raw")]
+    shown = " ".join(["python3", *cmd[1:7]])
+    src = {"source": "this run", "command": shown + " (summaries in a temporary directory)",
+           "kernel_build_sha256": fingerprint(os.path.basename(FWD_SOURCE))}
+    try:
+        r = subprocess.run(cmd, cwd=ROOT, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=limit_s)
+        if r.returncode != 0:
+            src["error"] = f"harness exit {r.returncode}: {r.stdout[-400:]}"
+            return None, None, src
+        traffic = counters = None
+        tf = recorded_fields(os.path.join(tmp, "out", os.path.basename(TRAFFIC_FILE)), w)
+        if tf is not None:
+            traffic = float(tf["hbm_bytes_per_launch"])
+        cf = recorded_fields(os.path.join(tmp, "out", os.path.basename(COUNTERS_FILE) if w.name == "ring_share_128k"
+                                          else f"attn_fwd_bf16_counters_{w.name}.txt"), w)
+        if cf is not None:
+            counters = {k: float(cf[k]) for k in ("mfma_busy_frac", "mfma_flop_per_algorithmic_flop",
+                                                 "valu_coexec_frac_of_mfma_busy", "lds_bank_conflict_frac",
+                                                 "effective_sclk_ghz")}
+        return traffic, counters, src
+    except Exception as e:   # no profiler, a time limit, unreadable output: fall back to the recorded figures
+        src["error"] = f"{type(e).__name__}: {e}"
+        return None, None, src
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -621,6 +667,8 @@ def main():
     ap.add_argument("--no-ffn", action="store_true",
                     help="skip the blockwise feed-forward leg (run with the ring-share workload only)")
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
+    ap.add_argument("--no-live-counters", action="store_true",
+                    help="report the recorded traffic and counters instead of measuring them with the harness")
     ap.add_argument("--clock-seconds", type=float, default=CLOCK_SECONDS,
                     help="length of the run after each timed region over which clock and power are sampled (0: none)")
     ap.add_argument("--no-ulysses", action="store_true",
@@ -787,6 +835,22 @@ def main():
         if out["ulysses"] is not None:
             log("timing the CPU oracle on the Ulysses share's seeded rows")
             out["ulysses"]["cpu_baseline"] = cpu_baseline_sampled_rows(W.WORKLOADS["ulysses_share_256k"])
+    if not args.no_live_counters:
+        log("measuring traffic and matrix-core counters with the rocprofv3 harness (child processes)")
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        traffic, ctrs, src = live_counters(w)
+        log(f"live counters: traffic {traffic}, counters {ctrs}, source {src}")
+        if traffic is not None:
+            out["roofline"]["traffic"] = traffic
+            out["traffic_source"] = src
+        elif out["traffic_source"] is not None and "error" in src:
+            out["traffic_source"]["live_error"] = src["error"]
+        if ctrs is not None:
+            out["counters"] = ctrs
+            out["counters_source"] = src
+        elif out["counters_source"] is not None and "error" in src:
+            out["counters_source"]["live_error"] = src["error"]
     print(json.dumps(out), flush=True)
 
 

@@ -78,7 +78,8 @@ def run_profiled(tag: str, prof_args: list[str], bench_args: list[str], raw: str
     shutil.rmtree(out, ignore_errors=True)
     os.makedirs(out, exist_ok=True)
     if "--calibrate-copy" not in bench_args:
-        bench_args = [*bench_args, "--clock-seconds", "0"]   # no clock/power run after the profiled steps
+        # no clock/power run after the profiled steps, and no nested harness run
+        bench_args = [*bench_args, "--clock-seconds", "0", "--no-live-counters"]
     cmd = ["timeout", "-s", "KILL", str(limit), rocprof(), *prof_args, "--output-format", "csv", "-d", out, "-o", "run",
            "--", sys.executable, BENCH, *bench_args]
     shown = " ".join(["timeout", "-s", "KILL", str(limit), "rocprofv3", *prof_args, "--output-format", "csv", "-d",
