@@ -609,7 +609,7 @@ def recorded_counters(w):
         return None
 
 
-def live_counters(w, limit_s: int = 420):
+def live_counters(w, limit_s: int = 240):
     """Traffic and matrix-core counters of this workload's forward launches measured in this run: the committed
     rocprofv3 harness (python -m exact_blockwise_attention_fwd_amd.profile) runs as a child process once this
     process has finished its own GPU work, each profiled bench step a grandchild under its own time limit.
@@ -633,9 +633,20 @@ def live_counters(w, limit_s: int = 420):
     src = {"source": "this run", "command": shown + " (summaries in a temporary directory)",
            "kernel_build_sha256": fingerprint(os.path.basename(FWD_SOURCE))}
     try:
-        r = subprocess.run(cmd, cwd=ROOT, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=limit_s)
-        if r.returncode != 0:
-            src["error"] = f"harness exit {r.returncode}: {r.stdout[-400:]}"
+        # its own session, so that a time limit ends the harness and every profiled grandchild together
+        p = subprocess.Popen(cmd, cwd=ROOT, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True,
+                             start_new_session=True)
+        try:
+            stdout, _ = p.communicate(timeout=limit_s)
+        except subprocess.TimeoutExpired:
+            import signal
+
+            os.killpg(p.pid, signal.SIGKILL)
+            p.communicate()
+            src["error"] = f"harness did not finish within {limit_s} s"
+            return None, None, src
+        if p.returncode != 0:
+            src["error"] = f"harness exit {p.returncode}: {stdout[-400:]}"
             return None, None, src
         traffic = counters = None
         tf = recorded_fields(os.path.join(tmp, "out", os.path.basename(TRAFFIC_FILE)), w)
